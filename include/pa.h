@@ -1,0 +1,200 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache attention library.
+ *
+ * The library implements the attention step of a nano-vLLM-style inference
+ * engine over a paged KV cache: storing this step's K/V rows through a slot
+ * mapping, variable-length causal prefill, and batched single-token decode
+ * with a split-K (flash-decoding) partition plus a reduce.
+ *
+ * Sources (web pages describing the method):
+ *   [Intro]   "大模型推理入门与 nano-vLLM 源码详解" (duanmeng.github.io)
+ *   [Pico #6] "Pico-vLLM 开发日志 #6" on Fain's blog (koas-w.github.io)
+ *   [Log-walk] "对着日志读懂 nano-vllm" (juejin.cn)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named *_cache, q, k, v, out, workspace, slot_mapping,
+ *   block_table, context_lens, cu_seqlens_* are DEVICE pointers; every other
+ *   argument is a host value.  The caller owns all memory (the library never
+ *   allocates, frees, synchronises, or reads device memory from the host).
+ *   All work is enqueued on `stream` (may be 0 for the null stream); launch
+ *   shapes depend only on host arguments, so calls can be captured in a HIP
+ *   graph.
+ * - KV cache layout (one layer's slice of the engine pool [Intro §11.5]):
+ *   k_cache, v_cache are contiguous [num_blocks, block_size, num_kv_heads,
+ *   head_dim] arrays of `dtype`.  Slot s is block s / block_size, offset
+ *   s % block_size [Intro §9.2].
+ * - dtype: PA_DTYPE_F32 or PA_DTYPE_BF16.  q, k, v, caches and out all share
+ *   it.  Arithmetic is fp32 throughout; outputs are rounded to `dtype`
+ *   (round to nearest even for bf16).
+ * - head_dim in {64, 128}; block_size a power of two in [8, 1024];
+ *   num_q_heads a multiple of num_kv_heads with a group size
+ *   num_q_heads / num_kv_heads in {1, 2, 4, 8}.  Query head h reads kv head
+ *   h / group (consecutive query heads share a kv head [Intro §19.6]).
+ * - Strides are in elements; the innermost (head_dim) stride is always 1.
+ *   Vector loads need 16-byte alignment of device pointers and of
+ *   stride * sizeof(dtype); pa_store_kv falls back to element copies when a
+ *   source is not aligned, the other entry points reject misalignment.
+ * - Device-resident values are not validated: slots, block-table entries,
+ *   lengths and cu_seqlens must be in range, else the behaviour is undefined.
+ *   Documented sentinels: slot -1 (no write), block-table entries past a
+ *   sequence's ceil(len / block_size) blocks (never read, so -1 padding is
+ *   legal), context_len 0 (output zeros).
+ * - Return value: PA_OK, or a negative PA_ERR_* code.  Argument checks run on
+ *   the host before any launch; a failed launch returns PA_ERR_LAUNCH.
+ *   pa_strerror() names a code.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shape */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim, block_size, group, dtype or alignment */
+  PA_ERR_WORKSPACE = -3,   /* workspace too small for the requested split */
+  PA_ERR_LAUNCH = -4       /* the HIP runtime reported a launch error */
+};
+
+enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+/* Static description of a status code. */
+const char* pa_strerror(int status);
+
+/*
+ * pa_store_kv -- write this step's K and V rows into the paged cache.
+ *
+ * Defined by [Intro §13.1] and the store of [Pico #6]: for each new token i
+ * with s = slot_mapping[i] != -1, copy k[i, h, :] to
+ * k_cache[s / block_size, s % block_size, h, :] for every kv head h, and the
+ * same for v.  A slot of -1 is a padding row [Intro §13.5] and writes nothing.
+ * The copy is bitwise (NaN payloads, signed zeros survive).
+ *
+ *   k, v               [num_tokens, num_kv_heads, head_dim], token strides
+ *                      k_tok_stride / v_tok_stride and head strides
+ *                      k_head_stride / v_head_stride (elements, may describe a
+ *                      view into a fused QKV buffer [Pico #6, pitfall 1]).
+ *   k_cache, v_cache   as in the conventions; num_blocks physical blocks.
+ *   slot_mapping       int32 [num_tokens]; unique slots in
+ *                      [0, num_blocks * block_size), or -1.
+ * num_tokens == 0 is a no-op.  Slots must not repeat within a call (which
+ * write wins would be unspecified).
+ */
+int pa_store_kv(const void* k, const void* v, int64_t k_tok_stride, int64_t k_head_stride,
+                int64_t v_tok_stride, int64_t v_head_stride, void* k_cache, void* v_cache,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                hipStream_t stream);
+
+/*
+ * pa_decode_workspace_size -- host-only helper for pa_decode.
+ *
+ * A decode of num_seqs sequences whose longest context is max_context_len,
+ * cut into splits of partition_tokens logical positions, uses
+ * num_splits = max(1, ceil(max_context_len / partition_tokens)) splits and a
+ * workspace of num_seqs * num_q_heads * num_splits * (head_dim + 2) floats:
+ *
+ *   acc [num_seqs, num_q_heads, num_splits, head_dim]   then
+ *   ml  [num_seqs, num_q_heads, num_splits, 2]
+ *
+ * acc is the split's un-normalised output sum_j 2^(t_j - m) v_j, ml holds
+ * m = max_j t_j and l = sum_j 2^(t_j - m), where t_j = scale * log2(e) * q.k_j
+ * is the score in base-2 units and j runs over the split's readable positions
+ * [Intro §9.5, §13.3].  Splits at or past a sequence's context are not written.
+ * partition_tokens must be a positive multiple of 64.
+ */
+int pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                             int32_t max_context_len, int32_t partition_tokens, size_t* bytes,
+                             int32_t* num_splits);
+
+/*
+ * pa_decode -- split-K partition pass of batched single-token decode.
+ *
+ * Defined by the decode path of [Intro §9.5, §11.4, §13.2] and the paged
+ * decode kernel of [Pico #6]: sequence b has context_lens[b] readable keys,
+ * including the token stored this step (so store before decode); query head h
+ * of sequence b attends, with weights softmax(scale * q.k_j), over positions
+ * 0..context_lens[b]-1 gathered through block_table[b].  This pass writes the
+ * per-split statistics described at pa_decode_workspace_size; pa_decode_reduce
+ * turns them into the output.
+ *
+ *   q             [num_seqs, num_q_heads, head_dim], strides q_seq_stride,
+ *                 q_head_stride.
+ *   block_table   int32 [num_seqs, >= ceil(max_context_len / block_size)]
+ *                 with row stride block_table_stride.
+ *   context_lens  int32 [num_seqs], each in [0, max_context_len].
+ *   workspace     float, at least the size pa_decode_workspace_size gives
+ *                 (workspace_bytes is checked).
+ */
+int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, int64_t block_table_stride,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+              int32_t max_context_len, int32_t partition_tokens, float scale, void* workspace,
+              size_t workspace_bytes, int32_t dtype, hipStream_t stream);
+
+/*
+ * pa_decode_reduce -- merge the splits written by pa_decode.
+ *
+ * [Intro §9.5]: with m* = max_s m_s, out = sum_s 2^(m_s - m*) acc_s /
+ * sum_s 2^(m_s - m*) l_s over the splits s < ceil(context_lens[b] /
+ * partition_tokens) -- never a sum of per-split normalised outputs.  A
+ * sequence with context_len 0 gets zeros.
+ *
+ *   out   [num_seqs, num_q_heads, head_dim] of dtype, strides out_seq_stride,
+ *         out_head_stride.
+ * num_splits and partition_tokens must be the values pa_decode used.
+ */
+int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t num_splits,
+                     int32_t partition_tokens, void* out, int64_t out_seq_stride,
+                     int64_t out_head_stride, int32_t dtype, hipStream_t stream);
+
+/*
+ * pa_prefill_varlen -- variable-length causal prefill over the paged cache.
+ *
+ * Defined by [Intro §10.2, §11.2, §13.2, §13.3]: sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (Lq rows) and Lk = cu_seqlens_k[b+1]
+ * - cu_seqlens_k[b] keys, read from the paged cache through block_table[b]
+ * (store this step's K/V first).  With c = Lk - Lq cached positions, query row
+ * i sits at position c + i and attends to positions 0..c+i (a causal mask
+ * aligned to the bottom-right).  Scores are scale * q.k in fp32; the softmax
+ * runs online in fp32; on bf16 inputs both matrix products run on bf16 MFMA
+ * tiles with the probabilities rounded to bf16 for the P.V product.
+ *
+ *   q, out        [total_q, num_q_heads, head_dim] (total_q = cu_seqlens_q[num_seqs]),
+ *                 strides q_tok_stride / q_head_stride, out_tok_stride /
+ *                 out_head_stride.
+ *   cu_seqlens_q, cu_seqlens_k  int32 [num_seqs + 1], non-decreasing, 0 first,
+ *                 with Lq <= Lk per sequence, Lq <= max_seqlen_q and
+ *                 Lk <= max_seqlen_k.
+ *   block_table   int32 [num_seqs, >= ceil(max_seqlen_k / block_size)],
+ *                 row stride block_table_stride.
+ * Supported: dtype bf16 (head_dim 64 or 128); PA_DTYPE_F32 returns
+ * PA_ERR_UNSUPPORTED.
+ */
+int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                      const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, const int32_t* block_table,
+                      int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, int32_t max_seqlen_q,
+                      int32_t max_seqlen_k, float scale, void* out, int64_t out_tok_stride,
+                      int64_t out_head_stride, int32_t dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,167 @@
+"""Python binding of the paged KV-cache attention library (libpa.so, gfx950).
+
+Argument marshalling only: every function here takes PyTorch device tensors,
+reads their pointers, sizes and strides, and calls the C entry point of the
+same name on the current HIP stream.  All computation happens in the HIP
+kernels of ``libpa.so``; there is no fallback.  The library is loaded on
+first use, and every entry point raises ``ImportError`` if it is not built
+(build it with ``python -m paged_kv_cache_114_amd._build`` or
+``__graft_entry__.build()``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_WORKSPACE = -3
+PA_ERR_LAUNCH = -4
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+
+EXPORTS = (
+    "pa_version",
+    "pa_strerror",
+    "pa_store_kv",
+    "pa_decode_workspace_size",
+    "pa_decode",
+    "pa_decode_reduce",
+    "pa_prefill_varlen",
+)
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m paged_kv_cache_114_amd._build")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.pa_version.restype = ctypes.c_int
+    lib.pa_version.argtypes = []
+    lib.pa_strerror.restype = ctypes.c_char_p
+    lib.pa_strerror.argtypes = [ctypes.c_int]
+    lib.pa_store_kv.restype = ctypes.c_int
+    lib.pa_store_kv.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, i32, i32, i32, i32, i64,
+                                i32, vp]
+    lib.pa_decode_workspace_size.restype = ctypes.c_int
+    lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz),
+                                             ctypes.POINTER(i32)]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, i64,
+                              i32, i32, f32, vp, sz, i32, vp]
+    lib.pa_decode_reduce.restype = ctypes.c_int
+    lib.pa_decode_reduce.argtypes = [vp, sz, vp, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp]
+    lib.pa_prefill_varlen.restype = ctypes.c_int
+    lib.pa_prefill_varlen.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                      i32, i32, i64, i32, i32, f32, vp, i64, i64, i32, vp]
+    return lib
+
+
+_LIB = None
+
+
+def library():
+    """The loaded ``libpa.so`` (ctypes handle); raises ImportError if it is not built."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def version() -> int:
+    return library().pa_version()
+
+
+def strerror(status: int) -> str:
+    return library().pa_strerror(status).decode()
+
+
+def _check(fn, status):
+    if status != PA_OK:
+        raise PAError(fn, status)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Store this step's K/V rows ``[T, Hkv, d]`` into ``[NB, bs, Hkv, d]`` caches."""
+    nb, bs, hkv, d = k_cache.shape
+    assert k.stride(-1) == 1 and v.stride(-1) == 1, "innermost stride must be 1"
+    _check("pa_store_kv", library().pa_store_kv(
+        _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1), _ptr(k_cache),
+        _ptr(v_cache), _ptr(slot_mapping), slot_mapping.shape[0], hkv, d, bs, nb,
+        _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                             partition_tokens):
+    """Returns ``(bytes, num_splits)`` of the decode workspace."""
+    nbytes = ctypes.c_size_t(0)
+    splits = ctypes.c_int32(0)
+    _check("pa_decode_workspace_size", library().pa_decode_workspace_size(
+        num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens,
+        ctypes.byref(nbytes), ctypes.byref(splits)))
+    return nbytes.value, splits.value
+
+
+def pa_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len, partition_tokens,
+              scale, workspace, stream=None) -> None:
+    """Partition pass: ``q [B, Hq, d]``; fills ``workspace`` (a float32 device tensor)."""
+    nb, bs, hkv, d = k_cache.shape
+    b, hq, _ = q.shape
+    _check("pa_decode", library().pa_decode(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        block_table.stride(0), _ptr(context_lens), b, hq, hkv, d, bs, nb, max_context_len,
+        partition_tokens, scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_decode_reduce(workspace, context_lens, num_splits, partition_tokens, out,
+                     stream=None) -> None:
+    """Merge the splits into ``out [B, Hq, d]``."""
+    b, hq, d = out.shape
+    _check("pa_decode_reduce", library().pa_decode_reduce(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(context_lens), b, hq,
+        d, num_splits, partition_tokens, _ptr(out), out.stride(0), out.stride(1),
+        _dtype_code(out), _stream(stream)))
+
+
+def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
+                      max_seqlen_q, max_seqlen_k, scale, out, stream=None) -> None:
+    """Causal varlen prefill: ``q, out [Tq, Hq, d]``; K/V read from the paged caches."""
+    nb, bs, hkv, d = k_cache.shape
+    tq, hq, _ = q.shape
+    _check("pa_prefill_varlen", library().pa_prefill_varlen(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), _ptr(block_table), block_table.stride(0), cu_seqlens_q.shape[0] - 1,
+        tq, hq, hkv, d, bs, nb, max_seqlen_q, max_seqlen_k, scale, _ptr(out), out.stride(0),
+        out.stride(1), _dtype_code(q), _stream(stream)))

@@ -1,0 +1,196 @@
+// C ABI entry points: host-side argument checks, then the launchers.
+// The contract of every function is documented in include/pa.h.
+
+#include "pa.h"
+
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(int32_t dtype) {
+  if (dtype == PA_DTYPE_F32) return 4;
+  if (dtype == PA_DTYPE_BF16) return 2;
+  return 0;
+}
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+bool block_size_ok(int32_t bs) { return is_pow2(bs) && bs >= 8 && bs <= 1024; }
+bool group_ok(int32_t hq, int32_t hkv) {
+  if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return false;
+  const int g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return kVersion; }
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape, dtype or alignment";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_store_kv(const void* k, const void* v, int64_t k_tok_stride, int64_t k_head_stride,
+                int64_t v_tok_stride, int64_t v_head_stride, void* k_cache, void* v_cache,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                hipStream_t stream) {
+  const int eb = elt_bytes(dtype);
+  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (k_tok_stride < 0 || k_head_stride < 0 || v_tok_stride < 0 || v_head_stride < 0)
+    return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (num_blocks > (INT32_MAX / block_size) + int64_t{1}) return PA_ERR_UNSUPPORTED;  // int32 slots
+  if (int64_t{num_tokens} * 2 * num_kv_heads * head_dim >= (int64_t{1} << 31))
+    return PA_ERR_UNSUPPORTED;
+  pa::StoreArgs a{k, v, k_tok_stride, k_head_stride, v_tok_stride, v_head_stride, k_cache,
+                  v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, eb};
+  return launched(pa::launch_store(a, stream));
+}
+
+int pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                             int32_t max_context_len, int32_t partition_tokens, size_t* bytes,
+                             int32_t* num_splits) {
+  if (!bytes || !num_splits) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (partition_tokens <= 0 || partition_tokens % 64 != 0) return PA_ERR_UNSUPPORTED;
+  int32_t s = (max_context_len + partition_tokens - 1) / partition_tokens;
+  if (s < 1) s = 1;
+  *num_splits = s;
+  *bytes = static_cast<size_t>(num_seqs) * num_q_heads * s * (head_dim + 2) * sizeof(float);
+  return PA_OK;
+}
+
+int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, int64_t block_table_stride,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+              int32_t max_context_len, int32_t partition_tokens, float scale, void* workspace,
+              size_t workspace_bytes, int32_t dtype, hipStream_t stream) {
+  const int eb = elt_bytes(dtype);
+  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_context_len < 0 || num_blocks <= 0 || block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!group_ok(num_q_heads, num_kv_heads)) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+      return PA_ERR_INVALID_ARG;
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_blocks > (int64_t{1} << 40)) return PA_ERR_UNSUPPORTED;
+  if (q_seq_stride < 0 || q_head_stride < 0 || block_table_stride < 0) return PA_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PA_ERR_INVALID_ARG;  // NaN scale
+  size_t need = 0;
+  int32_t splits = 0;
+  int st = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                    partition_tokens, &need, &splits);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !workspace)
+    return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (splits > 65535 || num_seqs > 65535) return PA_ERR_UNSUPPORTED;  // grid limits
+  if (!aligned16(q) || (q_seq_stride * eb) % 16 || (q_head_stride * eb) % 16 ||
+      !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+    return PA_ERR_UNSUPPORTED;
+  float* ws = static_cast<float*>(workspace);
+  const size_t acc_elems = static_cast<size_t>(num_seqs) * num_q_heads * splits * head_dim;
+  pa::DecodeArgs a{q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
+                   block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                   head_dim, block_size, partition_tokens, splits, scale, ws, ws + acc_elems,
+                   dtype == PA_DTYPE_BF16};
+  return launched(pa::launch_decode(a, stream));
+}
+
+int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t num_splits,
+                     int32_t partition_tokens, void* out, int64_t out_seq_stride,
+                     int64_t out_head_stride, int32_t dtype, hipStream_t stream) {
+  const int eb = elt_bytes(dtype);
+  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_splits <= 0) return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (partition_tokens <= 0 || partition_tokens % 64 != 0) return PA_ERR_UNSUPPORTED;
+  if (out_seq_stride < 0 || out_head_stride < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!workspace || !context_lens || !out) return PA_ERR_INVALID_ARG;
+  const size_t need =
+      static_cast<size_t>(num_seqs) * num_q_heads * num_splits * (head_dim + 2) * sizeof(float);
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(out) % eb) != 0)
+    return PA_ERR_UNSUPPORTED;
+  // Each lane writes head_dim / 64 adjacent elements with one store.
+  const int64_t lane_bytes = int64_t{head_dim} / 64 * eb;
+  if ((reinterpret_cast<uintptr_t>(out) % lane_bytes) || (out_seq_stride * eb) % lane_bytes ||
+      (out_head_stride * eb) % lane_bytes)
+    return PA_ERR_UNSUPPORTED;
+  const float* ws = static_cast<const float*>(workspace);
+  const size_t acc_elems = static_cast<size_t>(num_seqs) * num_q_heads * num_splits * head_dim;
+  pa::ReduceArgs a{ws, ws + acc_elems, context_lens, num_seqs, num_q_heads, head_dim, num_splits,
+                   partition_tokens, out, out_seq_stride, out_head_stride,
+                   dtype == PA_DTYPE_BF16};
+  return launched(pa::launch_reduce(a, stream));
+}
+
+int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                      const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, const int32_t* block_table,
+                      int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, int32_t max_seqlen_q,
+                      int32_t max_seqlen_k, float scale, void* out, int64_t out_tok_stride,
+                      int64_t out_head_stride, int32_t dtype, hipStream_t stream) {
+  const int eb = elt_bytes(dtype);
+  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_blocks <= 0 ||
+      block_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (max_seqlen_q > max_seqlen_k) return PA_ERR_INVALID_ARG;
+  if (!group_ok(num_q_heads, num_kv_heads)) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+      return PA_ERR_INVALID_ARG;
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (q_tok_stride < 0 || q_head_stride < 0 || out_tok_stride < 0 || out_head_stride < 0 ||
+      block_table_stride < 0)
+    return PA_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_table || !out)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (q_tok_stride * eb) % 16 || (q_head_stride * eb) % 16 || (out_tok_stride * eb) % 16 ||
+      (out_head_stride * eb) % 16)
+    return PA_ERR_UNSUPPORTED;
+  pa::PrefillArgs a{q, q_tok_stride, q_head_stride, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
+                    block_table, block_table_stride, num_seqs, num_q_heads, num_kv_heads,
+                    head_dim, block_size, max_seqlen_q, max_seqlen_k, scale, out,
+                    out_tok_stride, out_head_stride};
+  return launched(pa::launch_prefill(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,292 @@
+// Batched single-token decode over the paged KV cache: split-K partition pass
+// and the reduce that merges the splits.
+//
+// What is computed ("大模型推理入门与 nano-vLLM 源码详解" [Intro] §9.5, §11.4,
+// §13.3; "Pico-vLLM 开发日志 #6" [Pico #6], its paged decode kernel): for
+// sequence b and query head h, softmax(scale * q.k_j) weights over the
+// context_lens[b] readable positions j, gathered through block_table[b], times
+// v_j.  GQA: query heads g*G .. g*G+G-1 read kv head g [Intro §19.6].
+//
+// Design for gfx950:
+// * One wave owns one (sequence, kv head, split).  The G query heads of the
+//   GQA group are all held by that wave, so each K/V byte is read from HBM
+//   exactly once and feeds every query head that needs it.
+// * A head row (head_dim elements) is spread over kR lanes, 16 bytes each, so
+//   one wave load covers 64 / kR tokens with fully used 16-byte lanes; the kR
+//   partial dot products are combined with DPP row operations (no LDS).
+// * A tile issues kU such loads for K and for V before any arithmetic, so a
+//   wave keeps kU * 2 * 1 KiB in flight; several waves per SIMD cover HBM
+//   latency without software double buffering.
+// * The workgroup holds NW waves = NW consecutive kv heads of the same
+//   (sequence, split): together they read the contiguous part of each token's
+//   [num_kv_heads, head_dim] row, and they share one staged copy of the
+//   split's block-table entries in LDS.
+// * Online softmax in fp32, base-2 (scores pre-multiplied by log2 e and exp2
+//   on the hardware transcendental unit); the split statistics (m, l, acc)
+//   go to the workspace, and the reduce merges them as [Intro §9.5] requires.
+
+#include <math.h>
+
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+template <typename T, int D, int G>
+struct DecodeShape {
+  static constexpr int kE = Chunk<T>::kElems;  // elements per lane per load
+  static constexpr int kR = D / kE;            // lanes per head row
+  static constexpr int kTpl = kWave / kR;      // tokens per wave load
+  static constexpr int kU = G >= 4 ? 4 : 8;    // loads per tile, each for K and V
+  static constexpr int kTile = kTpl * kU;      // tokens per tile
+  static_assert(kR >= 1 && kR <= kWave && (kWave % kR) == 0, "row must fit a wave");
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T, int D, int G, int NW>
+__global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
+    const T* __restrict__ q, int64_t q_seq_stride, int64_t q_head_stride,
+    const T* __restrict__ k_cache, const T* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, int64_t bt_stride,
+    const int32_t* __restrict__ context_lens, int32_t num_kv_heads, int32_t bs_log2,
+    int32_t partition_tokens, int32_t num_splits, float scale_log2, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml) {
+  using S = DecodeShape<T, D, G>;
+  constexpr int kE = S::kE, kR = S::kR, kTpl = S::kTpl, kU = S::kU, kTile = S::kTile;
+  extern __shared__ int32_t bt_lds[];
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.z;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int g = blockIdx.y * NW + wave;
+
+  const int ctx = context_lens[b];
+  const int t0 = split * partition_tokens;
+  if (t0 >= ctx) return;  // empty split: nothing written, the reduce skips it
+  const int t1 = min(t0 + partition_tokens, ctx);
+
+  // Stage the block-table entries this split touches (shared by all waves).
+  const int first_blk = t0 >> bs_log2;
+  const int nblk = ((t1 - 1) >> bs_log2) - first_blk + 1;
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride + first_blk;
+  for (int i = threadIdx.x; i < nblk; i += NW * kWave) bt_lds[i] = bt_row[i];
+  __syncthreads();
+
+  const int row = lane / kR;  // which token of a wave load
+  const int col = lane % kR;  // which 16-byte chunk of the head row
+  const int num_q_heads = num_kv_heads * G;
+
+  float qf[G][kE];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const T* qp = q + static_cast<int64_t>(b) * q_seq_stride +
+                  static_cast<int64_t>(g * G + i) * q_head_stride + col * kE;
+    Chunk<T>::widen(load16(qp), qf[i]);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) qf[i][e] *= scale_log2;
+  }
+
+  float m[G], l[G], acc[G][kE];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[i][e] = 0.f;
+  }
+
+  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;
+  const T* kbase = k_cache + static_cast<int64_t>(g) * D + col * kE;
+  const T* vbase = v_cache + static_cast<int64_t>(g) * D + col * kE;
+  const int bs_mask = (1 << bs_log2) - 1;
+
+  for (int tb = t0; tb < t1; tb += kTile) {
+    uint4 kr[kU], vr[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = tb + u * kTpl + row;
+      if (j < t1) {
+        const int64_t blk = bt_lds[(j >> bs_log2) - first_blk];
+        const int64_t off = ((blk << bs_log2) + (j & bs_mask)) * slot_stride;
+        kr[u] = load16(kbase + off);
+        vr[u] = load16(vbase + off);
+      } else {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+
+    float sc[kU][G];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float kf[kE];
+      Chunk<T>::widen(kr[u], kf);
+      const bool valid = tb + u * kTpl + row < t1;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) d = fmaf(qf[i][e], kf[e], d);
+        d = group_sum<kR>(d);
+        sc[u][i] = valid ? d : -INFINITY;
+      }
+    }
+
+    float alpha[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float mt = sc[0][i];
+#pragma unroll
+      for (int u = 1; u < kU; ++u) mt = fmaxf(mt, sc[u][i]);
+      mt = across_groups_max<kR>(mt);
+      // The tile's first token (tb < t1) is valid, so mt and m_new are finite.
+      const float m_new = fmaxf(m[i], mt);
+      alpha[i] = fast_exp2(m[i] - m_new);
+      m[i] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        sc[u][i] = fast_exp2(sc[u][i] - m_new);
+        psum += sc[u][i];
+      }
+      l[i] = l[i] * alpha[i] + psum;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[i][e] *= alpha[i];
+    }
+
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float vf[kE];
+      Chunk<T>::widen(vr[u], vf);
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int e = 0; e < kE; ++e) acc[i][e] = fmaf(sc[u][i], vf[e], acc[i][e]);
+    }
+  }
+
+  // Combine the wave's token rows (all share the running maximum m).
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    l[i] = across_groups_sum<kR>(l[i]);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[i][e] = across_groups_sum<kR>(acc[i][e]);
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int64_t idx = (static_cast<int64_t>(b) * num_q_heads + g * G + i) * num_splits + split;
+      float4* dst = reinterpret_cast<float4*>(ws_acc + idx * D + col * kE);
+#pragma unroll
+      for (int e = 0; e < kE; e += 4)
+        dst[e / 4] = make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
+      if (col == 0) reinterpret_cast<float2*>(ws_ml)[idx] = make_float2(m[i], l[i]);
+    }
+  }
+}
+
+// One wave per (sequence, query head); each lane owns D / 64 output elements.
+template <typename T, int D>
+__global__ __launch_bounds__(4 * kWave) void decode_reduce_kernel(
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
+    const int32_t* __restrict__ context_lens, int32_t num_q_heads, int32_t num_splits,
+    int32_t partition_tokens, T* __restrict__ out, int64_t out_seq_stride,
+    int64_t out_head_stride) {
+  constexpr int kDpl = D / kWave;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int h = blockIdx.x * 4 + wave;
+  const int b = blockIdx.y;
+  if (h >= num_q_heads) return;
+  const int ctx = context_lens[b];
+  const int ns = min(num_splits, (ctx + partition_tokens - 1) / partition_tokens);
+  const int64_t base = (static_cast<int64_t>(b) * num_q_heads + h) * num_splits;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + base;
+
+  float m_star = -INFINITY;
+  for (int s = lane; s < ns; s += kWave) m_star = fmaxf(m_star, ml[s].x);
+  m_star = across_groups_max<1>(m_star);
+
+  float o[kDpl], lsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kDpl; ++k) o[k] = 0.f;
+  const float* acc = ws_acc + base * D + lane * kDpl;
+  for (int s = 0; s < ns; ++s) {
+    const float2 st = ml[s];
+    const float w = fast_exp2(st.x - m_star);
+    lsum = fmaf(w, st.y, lsum);
+#pragma unroll
+    for (int k = 0; k < kDpl; ++k) o[k] = fmaf(w, acc[static_cast<int64_t>(s) * D + k], o[k]);
+  }
+  const float inv = ns > 0 ? 1.f / lsum : 0.f;
+  T* dst = out + static_cast<int64_t>(b) * out_seq_stride + static_cast<int64_t>(h) * out_head_stride +
+           lane * kDpl;
+#pragma unroll
+  for (int k = 0; k < kDpl; ++k) {
+    const float val = ns > 0 ? o[k] * inv : 0.f;
+    if constexpr (sizeof(T) == 2)
+      reinterpret_cast<uint16_t*>(dst)[k] = f32_to_bf16_rne(val);
+    else
+      reinterpret_cast<float*>(dst)[k] = val;
+  }
+}
+
+template <typename T, int D, int G, int NW>
+hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
+  const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
+  const int max_blk = (a.partition_tokens + a.block_size - 1) / a.block_size + 1;
+  dim3 grid(a.num_splits, a.num_kv_heads / NW, a.num_seqs);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, NW>), grid, dim3(NW * kWave),
+                     max_blk * sizeof(int32_t), stream, static_cast<const T*>(a.q),
+                     a.q_seq_stride, a.q_head_stride, static_cast<const T*>(a.k_cache),
+                     static_cast<const T*>(a.v_cache), a.block_table, a.block_table_stride,
+                     a.context_lens, a.num_kv_heads, bs_log2, a.partition_tokens, a.num_splits,
+                     a.scale * kLog2e, a.ws_acc, a.ws_ml);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t pick_nw(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_kv_heads % 4 == 0) return run_partition<T, D, G, 4>(a, stream);
+  if (a.num_kv_heads % 2 == 0) return run_partition<T, D, G, 2>(a, stream);
+  return run_partition<T, D, G, 1>(a, stream);
+}
+
+template <typename T, int D>
+hipError_t pick_group(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return pick_nw<T, D, 1>(a, stream);
+    case 2: return pick_nw<T, D, 2>(a, stream);
+    case 4: return pick_nw<T, D, 4>(a, stream);
+    case 8: return pick_nw<T, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+hipError_t run_reduce(const ReduceArgs& a, hipStream_t stream) {
+  dim3 grid((a.num_q_heads + 3) / 4, a.num_seqs);
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), grid, dim3(4 * kWave), 0, stream, a.ws_acc,
+                     a.ws_ml, a.context_lens, a.num_q_heads, a.num_splits, a.partition_tokens,
+                     static_cast<T*>(a.out), a.out_seq_stride, a.out_head_stride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.head_dim == 128 ? pick_group<bf16_t, 128>(a, stream)
+                                       : pick_group<bf16_t, 64>(a, stream);
+  return a.head_dim == 128 ? pick_group<float, 128>(a, stream) : pick_group<float, 64>(a, stream);
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.head_dim == 128 ? run_reduce<bf16_t, 128>(a, stream)
+                                       : run_reduce<bf16_t, 64>(a, stream);
+  return a.head_dim == 128 ? run_reduce<float, 128>(a, stream) : run_reduce<float, 64>(a, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,66 @@
+// Launchers behind the C ABI (host side).  Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct StoreArgs {
+  const void* k;
+  const void* v;
+  int64_t k_tok_stride, k_head_stride, v_tok_stride, v_head_stride;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int32_t num_tokens, num_kv_heads, head_dim, block_size;
+  int32_t elt_bytes;  // 2 (bf16) or 4 (fp32)
+};
+hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  int64_t q_seq_stride, q_head_stride;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  int64_t block_table_stride;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
+  int32_t partition_tokens, num_splits;
+  float scale;
+  float* ws_acc;  // [B, Hq, S, D]
+  float* ws_ml;   // [B, Hq, S, 2]
+  bool bf16;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct ReduceArgs {
+  const float* ws_acc;
+  const float* ws_ml;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_q_heads, head_dim, num_splits, partition_tokens;
+  void* out;
+  int64_t out_seq_stride, out_head_stride;
+  bool bf16;
+};
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q;
+  int64_t q_tok_stride, q_head_stride;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const int32_t* block_table;
+  int64_t block_table_stride;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
+  int32_t max_seqlen_q, max_seqlen_k;
+  float scale;
+  void* out;
+  int64_t out_tok_stride, out_head_stride;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa
