@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input: for a
+decode workload, pa_store_kv (this step's K/V rows) -> pa_decode (split-K
+partition pass) -> pa_decode_reduce; for the prefill workload, pa_store_kv ->
+pa_prefill_varlen.  Inputs are resident in HBM before timing starts.  Before
+every step a 1 GiB buffer is read (outside the timed events) so the 256 MB
+Infinity Cache and the L2s hold no KV: a real engine touches 28 layers'
+caches between two visits to one layer.  The flush only reads, so it leaves
+no dirty lines whose write-back would steal bandwidth from the timed step.
+
+Default workload: the Qwen3-0.6B one-layer decode (batch 64, contexts uniform
+in [128, 1024], block 256, bf16).  `value` is its KV read rate: the K and V
+bytes the step must read (sum of context lengths x 8 kv heads x 128 x 2 x 2
+bytes) over the measured step time.  The JSON line also carries the roofline
+of the dominant kernel (decode partition pass), the oracle's CPU rate on a
+bounded sample, and (under "also") the heavy decode, the shared-prefix decode
+and the varlen prefill workloads measured the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, os.path.join(ROOT, "tests")):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+METRIC = "paged decode KV GB/s and % HBM peak; prefill TFLOP/s (% MFMA), Qwen3-0.6B"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FLUSH_BYTES = 1 << 30
+
+WORKLOAD_TEXT = {
+    "c2": "Qwen3-0.6B one-layer decode: batch 64, contexts U[128,1024], 16q/8kv heads, d=128, "
+          "bf16, block 256, shuffled blocks; store 64 new tokens then decode",
+    "c3": "Qwen3-0.6B one-layer varlen causal prefill: 8 sequences, lengths U[64,2048], 3 with "
+          "a 256/512-token cached prefix, 16q/8kv, d=128, bf16, block 256; store then prefill",
+    "c4": "heavy one-layer decode: batch 512, every context 4096, 16q/8kv, d=128, bf16, "
+          "block 256, random block placement",
+    "c5": "skewed shared-prefix decode: batch 256, block 16, 192 sequences share a 2048-token "
+          "prefix + lognormal tails (median 300, cap 6000), 64 private U[32,8192]",
+}
+
+
+def decode_partition(case, cus=256):
+    """Split size: enough (sequence, kv head, split) waves to give every CU several."""
+    waves = case.num_seqs * case.num_kv_heads
+    p = 64
+    while p < 8192 and waves * math.ceil(case.max_context_len / (2 * p)) >= 4 * cus * 4:
+        p *= 2
+    return p
+
+
+class Runner:
+    """Buffers and launches for one workload; times each step with HIP events."""
+
+    def __init__(self, name, partition=None):
+        import torch
+
+        import paged_kv_cache_114_amd as pa
+        import workloads as W
+        self.torch, self.pa, self.W = torch, pa, W
+        self.name = name
+        self.case = W.FULL_CASES[name]()
+        self.vals = W.materialize(self.case, "cuda:0")
+        c = self.case
+        self.kind = c.kind
+        if self.kind == "decode":
+            self.partition = partition or decode_partition(c)
+            nbytes, self.splits = pa.pa_decode_workspace_size(
+                c.num_seqs, c.num_q_heads, c.head_dim, c.max_context_len, self.partition)
+            self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+            self.out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=torch.bfloat16,
+                                   device="cuda:0")
+        else:
+            self.out = torch.empty_like(self.vals["q"])
+        self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        self.flush_sink = torch.zeros((), dtype=torch.float32, device="cuda:0")
+
+    def flush(self):
+        self.flush_sink.copy_(self.flush_buf.sum())
+
+    def step(self, ev):
+        pa, v, c = self.pa, self.vals, self.case
+        ev[0].record()
+        pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"], v["slot_mapping"])
+        ev[1].record()
+        if self.kind == "decode":
+            pa.pa_decode(v["q"], v["k_cache"], v["v_cache"], v["block_table"], v["context_lens"],
+                         c.max_context_len, self.partition, c.scale, self.ws)
+            ev[2].record()
+            pa.pa_decode_reduce(self.ws, v["context_lens"], self.splits, self.partition,
+                                self.out)
+        else:
+            pa.pa_prefill_varlen(v["q"], v["k_cache"], v["v_cache"], v["cu_seqlens_q"],
+                                 v["cu_seqlens_k"], v["block_table"], c.max_seqlen_q,
+                                 c.max_context_len, c.scale, self.out)
+            ev[2].record()
+        ev[3].record()
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for _ in range(warmup):
+            self.flush()
+            self.step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.flush()
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+        store_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        main_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        return dict(step_ms=sum(step_ms) / steps, store_ms=sum(store_ms) / steps,
+                    main_ms=sum(main_ms) / steps, min_step_ms=min(step_ms),
+                    wall_ms_per_step=1e3 * wall / steps)
+
+    # algorithmic work -------------------------------------------------------------
+    def kv_bytes(self):
+        return self.case.kv_bytes_logical()
+
+    def prefill_flops(self):
+        c = self.case
+        return 4 * c.head_dim * c.num_q_heads * c.causal_pairs()
+
+    def summary(self, t):
+        c = self.case
+        if self.kind == "decode":
+            logical = self.kv_bytes()
+            unique = c.kv_bytes_unique()
+            rate = logical / (t["step_ms"] * 1e-3) / 1e9
+            kern = logical / (t["main_ms"] * 1e-3) / 1e9
+            out = {"workload": c.name, "kv_GBps_step": round(rate, 1),
+                   "decode_kernel_GBps": round(kern, 1),
+                   "decode_kernel_frac_hbm": round(kern / HBM_PEAK_GBS, 4),
+                   "ms_per_step": round(t["step_ms"], 5),
+                   "decode_kernel_ms": round(t["main_ms"], 5),
+                   "partition_tokens": self.partition, "num_splits": self.splits}
+            if unique != logical:
+                out["unique_kv_GBps_kernel"] = round(unique / (t["main_ms"] * 1e-3) / 1e9, 1)
+                out["unique_frac_hbm"] = round(unique / (t["main_ms"] * 1e-3) / 1e9 /
+                                               HBM_PEAK_GBS, 4)
+            return out
+        flops = self.prefill_flops()
+        tf = flops / (t["main_ms"] * 1e-3) / 1e12
+        return {"workload": c.name, "prefill_TFLOPs_kernel": round(tf, 2),
+                "frac_bf16_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                "ms_per_step": round(t["step_ms"], 5), "prefill_kernel_ms": round(t["main_ms"], 5),
+                "gflop": round(flops / 1e9, 3)}
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """The oracle, untuned, on host copies of the same inputs: store + attention for
+    as many sequences as fit in the time budget (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from pa_runner import HostInputs
+
+    case = W.FULL_CASES[name]()
+    vals = W.materialize(case, "cuda:0")
+    order = list(np.random.default_rng(0).permutation(case.num_seqs))
+    done, elapsed, work = [], 0.0, 0
+    with threadpool_limits(limits=1):
+        while order and elapsed < budget_s:
+            chunk = [int(order.pop()) for _ in range(min(4, len(order)))]
+            host = HostInputs(case, vals, chunk)
+            t0 = time.perf_counter()
+            if case.kind == "decode":
+                host.decode()
+            else:
+                host.prefill()
+            elapsed += time.perf_counter() - t0
+            done += chunk
+    c = case
+    if case.kind == "decode":
+        work = 2 * c.num_kv_heads * c.head_dim * c.elt_bytes * int(c.context_lens[done].sum())
+        value, unit = work / elapsed / 1e9, "GB/s"
+    else:
+        pairs = 0
+        for b in done:
+            lq, lk = int(c.q_lens[b]), int(c.context_lens[b])
+            pairs += lq * (lk - lq + 1) + lq * (lq - 1) // 2
+        value, unit = 4 * c.head_dim * c.num_q_heads * pairs / elapsed / 1e12, "TFLOP/s"
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(value, 4), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {c.num_seqs} sequences of {c.name} (store + attention, "
+                      f"fp64 NumPy, 1 BLAS thread), {elapsed:.1f} s",
+            "cpu": cpu, "seconds": round(elapsed, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--no-also", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+                         "(decode shards by sequence or kv head with no exchange; see the "
+                         "design notes). Run with --gpus 1.\n")
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    main_run = Runner(args.workload, args.partition)
+    t = main_run.run(args.steps, args.warmup)
+    summ = main_run.summary(t)
+    c = main_run.case
+    if main_run.kind == "decode":
+        value = main_run.kv_bytes() / (t["step_ms"] * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = main_run.kv_bytes() / (t["main_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_partition_kernel",
+                "kernel_ms": round(t["main_ms"], 5)}
+    else:
+        value = main_run.prefill_flops() / (t["step_ms"] * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = main_run.prefill_flops() / (t["main_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel": "prefill_kernel", "kernel_ms": round(t["main_ms"], 5)}
+    del main_run
+    torch.cuda.empty_cache()
+
+    also = {}
+    if not args.no_also:
+        for name in ("c4", "c5", "c3"):
+            if name == args.workload:
+                continue
+            try:
+                r = Runner(name)
+                also[name] = r.summary(r.run(max(5, args.steps // 2), 3))
+                del r
+                torch.cuda.empty_cache()
+            except Exception as e:  # a workload whose kernel is missing is reported as such
+                also[name] = {"error": f"{type(e).__name__}: {e}"}
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t["step_ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values, random block placement)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "case": c.name,
+                   "batch": c.num_seqs, "max_context": c.max_context_len,
+                   "block_size": c.block_size, "q_heads": c.num_q_heads,
+                   "kv_heads": c.num_kv_heads, "head_dim": c.head_dim,
+                   "parallelism": "single GPU"},
+        "timing": {"store_ms": round(t["store_ms"], 5), "main_kernel_ms": round(t["main_ms"], 5),
+                   "min_step_ms": round(t["min_step_ms"], 5),
+                   "wall_ms_per_step_incl_cache_flush": round(t["wall_ms_per_step"], 4)},
+        "roofline": roof,
+        "detail": summ,
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

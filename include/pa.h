@@ -170,8 +170,9 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
  * (store this step's K/V first).  With c = Lk - Lq cached positions, query row
  * i sits at position c + i and attends to positions 0..c+i (a causal mask
  * aligned to the bottom-right).  Scores are scale * q.k in fp32; the softmax
- * runs online in fp32; on bf16 inputs both matrix products run on bf16 MFMA
- * tiles with the probabilities rounded to bf16 for the P.V product.
+ * runs online in fp32; both matrix products run on bf16 MFMA tiles, the
+ * probabilities entering P.V as a bf16 head plus a bf16 remainder (about 16
+ * significant bits).
  *
  *   q, out        [total_q, num_q_heads, head_dim] (total_q = cu_seqlens_q[num_seqs]),
  *                 strides q_tok_stride / q_head_stride, out_tok_stride /
