@@ -8,6 +8,7 @@
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kPrefillMaxTableEntries = 16384;
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -177,8 +178,11 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
   if (q_tok_stride < 0 || q_head_stride < 0 || out_tok_stride < 0 || out_head_stride < 0 ||
       block_table_stride < 0)
     return PA_ERR_INVALID_ARG;
-  if (!(scale == scale)) return PA_ERR_INVALID_ARG;
+  if (!(scale > 0.f)) return PA_ERR_INVALID_ARG;  // also rejects NaN
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  // the sequence's block-table entries are staged in LDS next to two K/V tiles
+  if ((max_seqlen_k + int64_t{block_size} - 1) / block_size > kPrefillMaxTableEntries)
+    return PA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_table || !out)
     return PA_ERR_INVALID_ARG;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;

@@ -29,8 +29,15 @@
 //   a 2e-3 absolute error bound.  This costs half again the MFMA work.
 // * LDS rows are padded by 16 bytes so the 16-byte reads of 32 consecutive
 //   rows fall in distinct banks.
-// * The next K/V tile is fetched from HBM into registers while the current
-//   one is being multiplied (register prefetch, one tile ahead).
+// * K/V tiles are double-buffered in LDS: while the MFMAs read one buffer,
+//   the tile after it (fetched from HBM into registers one tile earlier) is
+//   written into the other, so each tile costs one barrier.
+// * The sequence's block-table entries are staged in LDS once, so a K/V
+//   address never waits on a global load.
+// * The output is rescaled only when a tile's maximum score exceeds the
+//   reference maximum by more than 8 in base-2 units (lazy rescaling);
+//   otherwise the probabilities are taken against the old reference and stay
+//   below 2^8.
 // * Query tiles are dispatched heaviest first: blockIdx.z counts tiles back
 //   from the end of each sequence, and the last tiles see the most keys.
 
@@ -75,7 +82,7 @@ __device__ __forceinline__ int vt_slot_of_quad(int quad) {  // first slot of key
 }
 
 template <int D, int G>
-__global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel(
+__global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_tok_stride, int64_t q_head_stride,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
@@ -83,8 +90,10 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel
     int32_t bs_log2, float scale_log2, uint16_t* __restrict__ out, int64_t out_tok_stride,
     int64_t out_head_stride) {
   using S = PrefillShape<D, G>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * S::kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * S::kVRow];
+  // Two K/V tile buffers: one is read by the MFMAs while the other is filled.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * S::kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * S::kVRow];
+  extern __shared__ int32_t bt_lds[];  // this sequence's block-table entries
 
   const int g = blockIdx.x;
   const int b = blockIdx.y;
@@ -111,6 +120,15 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel
   const int my_pos = ctx0 + my_row;                         // its position in the sequence
   const int w_last_pos = ctx0 + min(lq - 1, w_q0 + 31);     // last position the wave needs
 
+  // Only keys 0..wg_last_pos are ever loaded (later keys of the last tile are in
+  // every row's future and stay zero in LDS), so the entries of blocks
+  // 0..wg_last_pos / block_size are all the tile needs.
+  {  // the block-table entries the tile's keys use, staged once
+    const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride;
+    const int n_bt = (wg_last_pos >> bs_log2) + 1;
+    for (int i = tid; i < n_bt; i += S::kThreads) bt_lds[i] = bt_row[i];
+  }
+
   // Q^T fragments: lane (half, col) holds dims s*16 + 8*half .. +7 of query row col.
   bf16x8_t qf[S::kSteps];
   {
@@ -120,12 +138,12 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel
     for (int s = 0; s < S::kSteps; ++s)
       qf[s] = as_bf16x8(row_ok ? load16(qp + 16 * s) : make_uint4(0, 0, 0, 0));
   }
+  __syncthreads();  // bt_lds ready
 
-  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride;
   const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;
   const int bs_mask = (1 << bs_log2) - 1;
   auto row_ptr = [&](const uint16_t* cache, int pos) {
-    const int64_t blk = bt_row[pos >> bs_log2];
+    const int64_t blk = bt_lds[pos >> bs_log2];
     return cache + ((blk << bs_log2) + (pos & bs_mask)) * slot_stride + static_cast<int64_t>(g) * D;
   };
 
@@ -137,8 +155,9 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel
       const int c = tid + i * S::kThreads;
       const int key = c / (D / 8), chunk = c % (D / 8);
       const int pos = kt0 + key;
-      kreg[i] = (c < S::kKChunks && pos < lk) ? load16(row_ptr(k_cache, pos) + 8 * chunk)
-                                              : make_uint4(0, 0, 0, 0);
+      kreg[i] = (c < S::kKChunks && pos <= wg_last_pos)
+                    ? load16(row_ptr(k_cache, pos) + 8 * chunk)
+                    : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < S::kVPer; ++i) {
@@ -147,18 +166,19 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pos = kt0 + 4 * quad + r;
-        vreg[i][r] = (gi < S::kVGroups && pos < lk) ? load16(row_ptr(v_cache, pos) + 8 * chunk)
-                                                    : make_uint4(0, 0, 0, 0);
+        vreg[i][r] = (gi < S::kVGroups && pos <= wg_last_pos)
+                         ? load16(row_ptr(v_cache, pos) + 8 * chunk)
+                         : make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < S::kKPer; ++i) {
       const int c = tid + i * S::kThreads;
       if (c < S::kKChunks) {
         const int key = c / (D / 8), chunk = c % (D / 8);
-        *reinterpret_cast<uint4*>(&k_lds[key * S::kKRow + 8 * chunk]) = kreg[i];
+        *reinterpret_cast<uint4*>(&k_lds[buf][key * S::kKRow + 8 * chunk]) = kreg[i];
       }
     }
 #pragma unroll
@@ -178,8 +198,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel
           const uint2 hi = make_uint2((w0[j] >> 16) | (w1[j] & 0xffff0000u),
                                       (w2[j] >> 16) | (w3[j] & 0xffff0000u));
           const int dim = 8 * chunk + 2 * j;
-          *reinterpret_cast<uint2*>(&vt_lds[dim * S::kVRow + slot]) = lo;
-          *reinterpret_cast<uint2*>(&vt_lds[(dim + 1) * S::kVRow + slot]) = hi;
+          *reinterpret_cast<uint2*>(&vt_lds[buf][dim * S::kVRow + slot]) = lo;
+          *reinterpret_cast<uint2*>(&vt_lds[buf][(dim + 1) * S::kVRow + slot]) = hi;
         }
       }
     }
@@ -188,76 +208,96 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads)) void prefill_kernel
   f32x16_t acc_o[S::kDB];
 #pragma unroll
   for (int db = 0; db < S::kDB; ++db) acc_o[db] = f32x16_t{};
-  float m_run = -INFINITY;  // running max of raw scores for this lane's query
-  float l_run = 0.f;        // this lane's share of the exponential sum
+  // Reference maximum (base-2 scaled units) of this lane's query.  It is raised
+  // only when a tile's maximum exceeds it by more than kLazy, so the output is
+  // rescaled rarely; meanwhile p = 2^(t - m_ref) stays below 2^kLazy.
+  constexpr float kLazy = 8.f;
+  float m_ref = -INFINITY;
+  float l_run = 0.f;  // this lane's share of the exponential sum
 
   fetch(0);
+  stage(0);
+  __syncthreads();
+  if (n_kt > 1) fetch(kBN);
   for (int kt = 0; kt < n_kt; ++kt) {
     const int kt0 = kt * kBN;
-    __syncthreads();  // every wave is done reading the previous tile
-    stage();
-    __syncthreads();
-    if (kt + 1 < n_kt) fetch(kt0 + kBN);
-    if (kt0 > w_last_pos) continue;  // the whole tile lies in this wave's future
-
-    f32x16_t acc_s[2];
+    const int buf = kt & 1;
+    if (kt0 <= w_last_pos) {  // otherwise the whole tile lies in this wave's future
+      f32x16_t acc_s[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      acc_s[mb] = f32x16_t{};
-      const uint16_t* kp = &k_lds[(mb * 32 + col) * S::kKRow + 8 * half];
+      for (int mb = 0; mb < 2; ++mb) {
+        acc_s[mb] = f32x16_t{};
+        const uint16_t* kp = &k_lds[buf][(mb * 32 + col) * S::kKRow + 8 * half];
 #pragma unroll
-      for (int s = 0; s < S::kSteps; ++s)
-        acc_s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * s)), qf[s], acc_s[mb], 0, 0, 0);
-    }
+        for (int s = 0; s < S::kSteps; ++s)
+          acc_s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * s)), qf[s], acc_s[mb], 0, 0,
+              0);
+      }
 
-    // causal mask on tiles that reach past the wave's first position
-    if (kt0 + kBN - 1 > ctx0 + w_q0) {
+      // causal mask on tiles that reach past the wave's first position
+      if (kt0 + kBN - 1 > ctx0 + w_q0) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt0 + mb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+            if (key > my_pos) acc_s[mb][r] = -INFINITY;
+          }
+      }
+
+      float tmax = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt0 + mb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          if (key > my_pos) acc_s[mb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc_s[mb][r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;  // scale_log2 > 0
+      if (__ballot(tmax > m_ref + kLazy)) {  // wave-uniform: raise the reference
+        const float m_new = fmaxf(m_ref, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < S::kDB; ++db) acc_o[db] *= alpha;
+      }
+
+      // p = 2^(t - m_ref) as a bf16 head (truncated) plus a bf16 remainder
+      float psum = 0.f;
+      bf16x8_t pf_hi[4], pf_lo[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -m_ref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r + 1], scale_log2, -m_ref));
+          psum += p0 + p1;
+          const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+          const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+          const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+          const uint32_t hi = (b0 >> 16) | (b1 & 0xffff0000u);
+          const uint32_t lo = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xffff0000u);
+          const int ks = 2 * mb + r / 8, e = r % 8;
+          pf_hi[ks][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi));
+          pf_hi[ks][e + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi >> 16));
+          pf_lo[ks][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo));
+          pf_lo[ks][e + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo >> 16));
         }
-    }
-
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc_s[mb][r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-    const float mc = m_new * scale_log2;
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8_t pf_hi[4], pf_lo[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -mc));
-        psum += p;
-        const __bf16 hi = static_cast<__bf16>(p);
-        pf_hi[2 * mb + r / 8][r % 8] = hi;
-        pf_lo[2 * mb + r / 8][r % 8] = static_cast<__bf16>(p - static_cast<float>(hi));
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < S::kDB; ++db) acc_o[db] *= alpha;
+      l_run += psum;
 
 #pragma unroll
-    for (int db = 0; db < S::kDB; ++db) {
-      const uint16_t* vp = &vt_lds[(db * 32 + col) * S::kVRow + 8 * half];
+      for (int db = 0; db < S::kDB; ++db) {
+        const uint16_t* vp = &vt_lds[buf][(db * 32 + col) * S::kVRow + 8 * half];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t va = as_bf16x8(*reinterpret_cast<const uint4*>(vp + 16 * ks));
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf_hi[ks], acc_o[db], 0, 0, 0);
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf_lo[ks], acc_o[db], 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8_t va = as_bf16x8(*reinterpret_cast<const uint4*>(vp + 16 * ks));
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf_hi[ks], acc_o[db], 0, 0, 0);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf_lo[ks], acc_o[db], 0, 0, 0);
+        }
       }
     }
+    if (kt + 1 < n_kt) stage(buf ^ 1);  // the other buffer was last read one tile ago
+    __syncthreads();
+    if (kt + 2 < n_kt) fetch(kt0 + 2 * kBN);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
@@ -283,8 +323,9 @@ hipError_t run(const PrefillArgs& a, hipStream_t stream) {
   using S = PrefillShape<D, G>;
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
   const int tiles = (a.max_seqlen_q + S::kBM - 1) / S::kBM;
+  const size_t bt_bytes = static_cast<size_t>((a.max_seqlen_k + a.block_size - 1) >> bs_log2) * 4;
   dim3 grid(a.num_kv_heads, a.num_seqs, tiles);
-  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(S::kThreads), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(S::kThreads), bt_bytes, stream,
                      static_cast<const uint16_t*>(a.q), a.q_tok_stride, a.q_head_stride,
                      static_cast<const uint16_t*>(a.k_cache), static_cast<const uint16_t*>(a.v_cache),
                      a.cu_seqlens_q, a.cu_seqlens_k, a.block_table, a.block_table_stride,

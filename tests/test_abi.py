@@ -153,3 +153,6 @@ def test_prefill_validation():
     assert prefill(d=80) == pa.PA_ERR_UNSUPPORTED
     assert prefill(hq=16, hkv=3) == pa.PA_ERR_INVALID_ARG
     assert prefill(bs=12) == pa.PA_ERR_UNSUPPORTED
+    assert prefill(scale=-0.5) == pa.PA_ERR_INVALID_ARG
+    assert prefill(scale=float("nan")) == pa.PA_ERR_INVALID_ARG
+    assert prefill(bs=8, mk=8 * 16384 + 1, mq=100) == pa.PA_ERR_UNSUPPORTED
