@@ -183,7 +183,7 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
  *   block_table   int32 [num_seqs, >= ceil(max_seqlen_k / block_size)],
  *                 row stride block_table_stride.
  * scale must be positive.  Supported: dtype bf16 (head_dim 64 or 128) and
- * ceil(max_seqlen_k / block_size) <= 16384; PA_DTYPE_F32 returns
+ * ceil(max_seqlen_k / block_size) <= 8192; PA_DTYPE_F32 returns
  * PA_ERR_UNSUPPORTED.
  */
 int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride,

@@ -8,7 +8,7 @@
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
-constexpr int64_t kPrefillMaxTableEntries = 16384;
+constexpr int64_t kPrefillMaxTableEntries = 8192;  // 32 KB of LDS beside the K/V tile buffers
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -180,6 +180,7 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
     return PA_ERR_INVALID_ARG;
   if (!(scale > 0.f)) return PA_ERR_INVALID_ARG;  // also rejects NaN
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  if (num_blocks > INT32_MAX / block_size) return PA_ERR_UNSUPPORTED;  // 32-bit slots
   // the sequence's block-table entries are staged in LDS next to two K/V tiles
   if ((max_seqlen_k + int64_t{block_size} - 1) / block_size > kPrefillMaxTableEntries)
     return PA_ERR_UNSUPPORTED;

@@ -19,19 +19,20 @@
 //   block, so the softmax max and sum are in-lane plus one exchange with the
 //   partner lane (lane ^ 32).
 // * O^T = V^T P^T: the probabilities feed the second MFMA straight from the
-//   score registers.  V is written to LDS transposed ([dim][key]) and with
-//   the keys of each 16-key group permuted to match the order in which the
-//   accumulator layout holds them, so every MFMA operand is a single 16-byte
-//   LDS read.
+//   score registers.  V stays row-major ([key][dim]) in LDS and each V^T
+//   operand is read with two ds_read_b64_tr_b16 (gfx950's transposing LDS
+//   read), whose per-16-lane transpose hands every lane 4 keys of one dim;
+//   the keys are chosen to match the order in which the score accumulator
+//   holds P, so no data is permuted anywhere.
 // * Each p is split into a bf16 head and a bf16 remainder (p - head) and both
 //   go through the P.V MFMA, so P carries ~16 significant bits instead of
 //   bf16's 8: with bf16 P alone, rows whose weighted values cancel can miss
 //   a 2e-3 absolute error bound.  This costs half again the MFMA work.
-// * LDS rows are padded by 16 bytes so the 16-byte reads of 32 consecutive
-//   rows fall in distinct banks.
-// * K/V tiles are double-buffered in LDS: while the MFMAs read one buffer,
-//   the tile after it (fetched from HBM into registers one tile earlier) is
-//   written into the other, so each tile costs one barrier.
+// * K/V tiles go from HBM straight into LDS by DMA (global_load_lds, 16 bytes
+//   a lane), double-buffered: the next tile streams in while the MFMAs read the
+//   current one, with no registers or VALU spent on staging and one barrier
+//   per tile.  Rows are XOR-swizzled by 16-byte chunk so an operand read of 32
+//   rows hits every bank group.
 // * The sequence's block-table entries are staged in LDS once, so a K/V
 //   address never waits on a global load.
 // * The output is rescaled only when a tile's maximum score exceeds the
@@ -43,6 +44,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -50,10 +53,15 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kBN = 64;   // keys per tile
-constexpr int kPad = 8;   // bf16 elements of row padding in LDS
+constexpr int kBN = 64;  // keys per tile
+// v_perm_b32 selector: perm(a, b, sel) picks bytes of {a:b} (b = bytes 0-3);
+// this one keeps the high halves: b.hi | a.hi << 16.
+constexpr uint32_t kPermHigh = 0x07060302u;
 
 template <int D, int G>
 struct PrefillShape {
@@ -63,22 +71,18 @@ struct PrefillShape {
   static constexpr int kBM = 32 * kRB;               // query positions per workgroup
   static constexpr int kSteps = D / 16;              // MFMA k-steps over head_dim
   static constexpr int kDB = D / 32;                 // 32-wide output blocks over head_dim
-  static constexpr int kKChunks = kBN * D / 8;       // 16-byte chunks of a K tile
-  static constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
-  static constexpr int kVGroups = (kBN / 4) * (D / 8);  // (4 keys x 8 dims) groups of a V tile
-  static constexpr int kVPer = (kVGroups + kThreads - 1) / kThreads;
-  static constexpr int kKRow = D + kPad;             // LDS row of K (elements)
-  static constexpr int kVRow = kBN + kPad;           // LDS row of V^T (elements)
+  static constexpr int kChunks = D / 8;              // 16-byte chunks per K/V row
+  static constexpr int kRowsPerDma = 1024 / (2 * D); // rows one wave-wide 1 KB DMA fills
+  static constexpr int kDmaPerTile = kBN / kRowsPerDma;
+  static constexpr int kDmaPerWave = kDmaPerTile / kWaves;
+  static_assert(kDmaPerTile % kWaves == 0, "DMA pieces must split evenly over the waves");
 };
+
+template <int B>
+struct Buf {};
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8_t, u);
-}
-
-// Position, within a group of 16 keys, at which key kk is stored in V^T so that
-// lane half h reads, for slots 8h..8h+7, the keys the score accumulator holds.
-__device__ __forceinline__ int vt_slot_of_quad(int quad) {  // first slot of keys 4q..4q+3
-  return 8 * (quad & 1) + 4 * (quad >> 1);
 }
 
 template <int D, int G>
@@ -90,9 +94,14 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     int32_t bs_log2, float scale_log2, uint16_t* __restrict__ out, int64_t out_tok_stride,
     int64_t out_head_stride) {
   using S = PrefillShape<D, G>;
-  // Two K/V tile buffers: one is read by the MFMAs while the other is filled.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * S::kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * S::kVRow];
+  // Two K/V tile buffers, row-major [key][dim], each row's 16-byte chunks
+  // XOR-swizzled by the row index: chunk c of row r sits at position
+  // c ^ (r mod kChunks), so reading one chunk column over 32 rows (an MFMA
+  // operand) touches every bank group instead of one.
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * D];
   extern __shared__ int32_t bt_lds[];  // this sequence's block-table entries
 
   const int g = blockIdx.x;
@@ -120,8 +129,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   const int my_pos = ctx0 + my_row;                         // its position in the sequence
   const int w_last_pos = ctx0 + min(lq - 1, w_q0 + 31);     // last position the wave needs
 
-  // Only keys 0..wg_last_pos are ever loaded (later keys of the last tile are in
-  // every row's future and stay zero in LDS), so the entries of blocks
+  // Only keys 0..wg_last_pos are ever loaded, so the entries of blocks
   // 0..wg_last_pos / block_size are all the tile needs.
   {  // the block-table entries the tile's keys use, staged once
     const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride;
@@ -140,70 +148,52 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   }
   __syncthreads();  // bt_lds ready
 
-  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;
+  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;  // elements per slot
   const int bs_mask = (1 << bs_log2) - 1;
   auto row_ptr = [&](const uint16_t* cache, int pos) {
     const int64_t blk = bt_lds[pos >> bs_log2];
     return cache + ((blk << bs_log2) + (pos & bs_mask)) * slot_stride + static_cast<int64_t>(g) * D;
   };
 
-  uint4 kreg[S::kKPer];
-  uint4 vreg[S::kVPer][4];
-  auto fetch = [&](int kt0) {
+  // A tile moves from HBM to LDS by DMA (global_load_lds): a wave-wide
+  // instruction writes 1 KB of LDS, lane l's 16 bytes at offset 16 l, so each
+  // lane fetches the source chunk that the swizzle places at its position.
+  // Keys past wg_last_pos are in the future of every row of the tile and get
+  // masked; they are fetched from position wg_last_pos (a readable row), so
+  // P.V only ever multiplies finite values.
+  auto dma = [&](const uint16_t* cache, uint16_t* lds, int kt0) {
 #pragma unroll
-    for (int i = 0; i < S::kKPer; ++i) {
-      const int c = tid + i * S::kThreads;
-      const int key = c / (D / 8), chunk = c % (D / 8);
-      const int pos = kt0 + key;
-      kreg[i] = (c < S::kKChunks && pos <= wg_last_pos)
-                    ? load16(row_ptr(k_cache, pos) + 8 * chunk)
-                    : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < S::kVPer; ++i) {
-      const int gi = tid + i * S::kThreads;
-      const int quad = gi % (kBN / 4), chunk = gi / (kBN / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = kt0 + 4 * quad + r;
-        vreg[i][r] = (gi < S::kVGroups && pos <= wg_last_pos)
-                         ? load16(row_ptr(v_cache, pos) + 8 * chunk)
-                         : make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < S::kDmaPerWave; ++i) {
+      const int piece = wave * S::kDmaPerWave + i;
+      const int row = piece * S::kRowsPerDma + lane / S::kChunks;
+      const int pos = lane % S::kChunks;
+      const int chunk = pos ^ (row & (S::kChunks - 1));
+      const uint16_t* src = row_ptr(cache, min(kt0 + row, wg_last_pos)) + 8 * chunk;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds + piece * 512), 16, 0,
+                                       0);
     }
   };
-  auto stage = [&](int buf) {
+
+  // Per-lane LDS offsets (elements) of the MFMA operands, fixed for the kernel.
+  // K operand (A of S^T = K Q^T): row mb*32 + col, chunk 2s + half.
+  int k_off[S::kSteps];
 #pragma unroll
-    for (int i = 0; i < S::kKPer; ++i) {
-      const int c = tid + i * S::kThreads;
-      if (c < S::kKChunks) {
-        const int key = c / (D / 8), chunk = c % (D / 8);
-        *reinterpret_cast<uint4*>(&k_lds[buf][key * S::kKRow + 8 * chunk]) = kreg[i];
-      }
+  for (int s = 0; s < S::kSteps; ++s)
+    k_off[s] = col * D + 8 * ((2 * s + half) ^ (col & (S::kChunks - 1)));
+  // V operand (A of O^T = V^T P^T) via transpose reads: for read t of step ks,
+  // lane (half, col) supplies the row of key ks*16 + 8t + 4 half + (col % 16) / 4
+  // and dims db*32 + 16 (col / 16) + 4 (col % 4) .. +3; the read hands it the
+  // keys ks*16 + 8t + 4 half + e (e = 0..3) of dim db*32 + col.
+  int v_off[2][S::kDB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db) {
+      const int key = 8 * t + 4 * half + (col % 16) / 4;
+      const int j4 = col % 4;
+      const int chunk = db * 4 + 2 * (col / 16) + j4 / 2;
+      v_off[t][db] = key * D + 8 * (chunk ^ (key & (S::kChunks - 1))) + 4 * (j4 % 2);
     }
-#pragma unroll
-    for (int i = 0; i < S::kVPer; ++i) {
-      const int gi = tid + i * S::kThreads;
-      if (gi < S::kVGroups) {
-        const int quad = gi % (kBN / 4), chunk = gi / (kBN / 4);
-        const int slot = 16 * (quad / 4) + vt_slot_of_quad(quad % 4);
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // dims 2j (low halves) and 2j+1 (high halves)
-          const uint2 lo = make_uint2((w0[j] & 0xffffu) | (w1[j] << 16),
-                                      (w2[j] & 0xffffu) | (w3[j] << 16));
-          const uint2 hi = make_uint2((w0[j] >> 16) | (w1[j] & 0xffff0000u),
-                                      (w2[j] >> 16) | (w3[j] & 0xffff0000u));
-          const int dim = 8 * chunk + 2 * j;
-          *reinterpret_cast<uint2*>(&vt_lds[buf][dim * S::kVRow + slot]) = lo;
-          *reinterpret_cast<uint2*>(&vt_lds[buf][(dim + 1) * S::kVRow + slot]) = hi;
-        }
-      }
-    }
-  };
 
   f32x16_t acc_o[S::kDB];
 #pragma unroll
@@ -215,89 +205,116 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the exponential sum
 
-  fetch(0);
-  stage(0);
-  __syncthreads();
-  if (n_kt > 1) fetch(kBN);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int kt0 = kt * kBN;
-    const int buf = kt & 1;
-    if (kt0 <= w_last_pos) {  // otherwise the whole tile lies in this wave's future
-      f32x16_t acc_s[2];
+  auto compute = [&](const uint16_t* kt_lds, const uint16_t* vt_lds, int kt0) {
+    // S^T = K Q^T: the two 32-key accumulator chains are interleaved.
+    f32x16_t acc_s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        acc_s[mb] = f32x16_t{};
-        const uint16_t* kp = &k_lds[buf][(mb * 32 + col) * S::kKRow + 8 * half];
-#pragma unroll
-        for (int s = 0; s < S::kSteps; ++s)
-          acc_s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(*reinterpret_cast<const uint4*>(kp + 16 * s)), qf[s], acc_s[mb], 0, 0,
-              0);
-      }
+    for (int s = 0; s < S::kSteps; ++s) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(kt_lds + k_off[s]);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(kt_lds + k_off[s] + 32 * D);
+      acc_s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[s], acc_s[0], 0, 0, 0);
+      acc_s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), qf[s], acc_s[1], 0, 0, 0);
+    }
 
-      // causal mask on tiles that reach past the wave's first position
-      if (kt0 + kBN - 1 > ctx0 + w_q0) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + mb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-            if (key > my_pos) acc_s[mb][r] = -INFINITY;
-          }
-      }
-
-      float tmax = -INFINITY;
+    // causal mask on tiles that reach past the wave's first position
+    if (kt0 + kBN - 1 > ctx0 + w_q0) {
+      const int lim = my_pos - kt0 - 4 * half;  // key index (within the tile, sans 4 half) limit
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc_s[mb][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;  // scale_log2 > 0
-      if (__ballot(tmax > m_ref + kLazy)) {  // wave-uniform: raise the reference
-        const float m_new = fmaxf(m_ref, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
+        for (int r = 0; r < 16; ++r)
+          if (mb * 32 + 8 * (r / 4) + (r % 4) > lim) acc_s[mb][r] = -INFINITY;
+    }
+
+    float tmax = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < S::kDB; ++db) acc_o[db] *= alpha;
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc_s[mb][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;  // scale_log2 > 0
+    if (__ballot(tmax > m_ref + kLazy)) {  // wave-uniform: raise the reference
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db) acc_o[db] *= alpha;
+    }
+
+    // p = 2^(t - m_ref) as a bf16 head (truncated) plus a bf16 remainder,
+    // packed two per word in the order the B operand of P.V wants
+    float psum = 0.f;
+    uint32_t w_hi[16], w_lo[16];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r + 1], scale_log2, -m_ref));
+        psum += p0 + p1;
+        const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+        const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+        const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+        w_hi[mb * 8 + r / 2] = __builtin_amdgcn_perm(b1, b0, kPermHigh);
+        w_lo[mb * 8 + r / 2] =
+            __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), kPermHigh);
       }
+    l_run += psum;
 
-      // p = 2^(t - m_ref) as a bf16 head (truncated) plus a bf16 remainder
-      float psum = 0.f;
-      bf16x8_t pf_hi[4], pf_lo[4];
+    // O^T += V^T P^T: kDB independent accumulator chains interleaved; each V
+    // operand (two transpose reads) serves the head and the remainder of P.
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -m_ref));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r + 1], scale_log2, -m_ref));
-          psum += p0 + p1;
-          const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-          const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
-          const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
-          const uint32_t hi = (b0 >> 16) | (b1 & 0xffff0000u);
-          const uint32_t lo = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xffff0000u);
-          const int ks = 2 * mb + r / 8, e = r % 8;
-          pf_hi[ks][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi));
-          pf_hi[ks][e + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi >> 16));
-          pf_lo[ks][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo));
-          pf_lo[ks][e + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo >> 16));
-        }
-      l_run += psum;
-
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t ph = as_bf16x8(
+          make_uint4(w_hi[4 * ks], w_hi[4 * ks + 1], w_hi[4 * ks + 2], w_hi[4 * ks + 3]));
+      const bf16x8_t pl = as_bf16x8(
+          make_uint4(w_lo[4 * ks], w_lo[4 * ks + 1], w_lo[4 * ks + 2], w_lo[4 * ks + 3]));
+      bf16x8_t va[S::kDB];
 #pragma unroll
       for (int db = 0; db < S::kDB; ++db) {
-        const uint16_t* vp = &vt_lds[buf][(db * 32 + col) * S::kVRow + 8 * half];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8_t va = as_bf16x8(*reinterpret_cast<const uint4*>(vp + 16 * ks));
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf_hi[ks], acc_o[db], 0, 0, 0);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf_lo[ks], acc_o[db], 0, 0, 0);
-        }
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(vt_lds + ks * 16 * D + v_off[0][db]));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(vt_lds + ks * 16 * D + v_off[1][db]));
+        va[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db)
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], ph, acc_o[db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < S::kDB; ++db)
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pl, acc_o[db], 0, 0, 0);
     }
-    if (kt + 1 < n_kt) stage(buf ^ 1);  // the other buffer was last read one tile ago
+  };
+
+  // One tile per iteration: start the DMA of the next tile into the other
+  // buffer (last read one iteration ago, and every wave has passed the barrier
+  // since), multiply the current one, then wait for this wave's DMA and meet
+  // at the barrier.  Buffers are chosen at compile time (the loop is unrolled
+  // by two) so the compiler can tell the DMA target from the buffer being read.
+  auto iteration = [&](int kt, auto buf) {
+    constexpr bool kFirst = std::is_same<decltype(buf), Buf<0>>::value;
+    const uint16_t* k_cur = kFirst ? k_lds0 : k_lds1;
+    const uint16_t* v_cur = kFirst ? v_lds0 : v_lds1;
+    uint16_t* k_nxt = kFirst ? k_lds1 : k_lds0;
+    uint16_t* v_nxt = kFirst ? v_lds1 : v_lds0;
+    const int kt0 = kt * kBN;
+    if (kt + 1 < n_kt) {
+      dma(k_cache, k_nxt, kt0 + kBN);
+      dma(v_cache, v_nxt, kt0 + kBN);
+    }
+    if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0);  // else: all in this wave's future
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 2 < n_kt) fetch(kt0 + 2 * kBN);
+  };
+
+  dma(k_cache, k_lds0, 0);
+  dma(v_cache, v_lds0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    iteration(kt, Buf<0>{});
+    if (kt + 1 < n_kt) iteration(kt + 1, Buf<1>{});
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
