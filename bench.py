@@ -162,6 +162,34 @@ class Runner:
                 "gflop": round(flops / 1e9, 3)}
 
 
+KERNEL_SOURCES = {
+    "decode_partition_kernel": ["paged_kv_cache_114_amd/csrc/pa_decode.hip",
+                                "paged_kv_cache_114_amd/csrc/pa_common.h"],
+    "prefill_kernel": ["paged_kv_cache_114_amd/csrc/pa_prefill.hip",
+                       "paged_kv_cache_114_amd/csrc/pa_common.h"],
+}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch (read + written) from the committed FETCH_SIZE / WRITE_SIZE
+    profile, or None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    with open(path) as fh:
+        rec = json.load(fh)
+    for e in rec["entries"]:
+        if e["workload"] == workload and e["kernel"] == kernel and e["source_hash"] == digest:
+            return int(round(e["read_bytes"] + e["write_bytes"]))
+    return None
+
+
 def cpu_baseline(name, budget_s=12.0):
     """The oracle, untuned, on host copies of the same inputs: store + attention for
     as many sequences as fit in the time budget (at least one)."""
@@ -219,6 +247,9 @@ def main():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--no-also", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run plain device copies of this size (a known-traffic kernel "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -230,6 +261,17 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return
+
     main_run = Runner(args.workload, args.partition)
     t = main_run.run(args.steps, args.warmup)
     summ = main_run.summary(t)
@@ -239,7 +281,10 @@ def main():
         unit = "GB/s"
         achieved = main_run.kv_bytes() / (t["main_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.workload, "decode_partition_kernel"),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                "algorithmic_bytes": main_run.kv_bytes(),
                 "kernel": "decode_partition_kernel",
                 "kernel_ms": round(t["main_ms"], 5)}
     else:
@@ -248,7 +293,10 @@ def main():
         achieved = main_run.prefill_flops() / (t["main_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": None, "kernel": "prefill_kernel", "kernel_ms": round(t["main_ms"], 5)}
+                "traffic": measured_traffic(args.workload, "prefill_kernel"),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                "algorithmic_flops": main_run.prefill_flops(),
+                "kernel": "prefill_kernel", "kernel_ms": round(t["main_ms"], 5)}
     del main_run
     torch.cuda.empty_cache()
 
