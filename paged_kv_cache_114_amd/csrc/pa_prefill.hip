@@ -31,8 +31,8 @@
 // * K/V tiles go from HBM straight into LDS by DMA (global_load_lds, 16 bytes
 //   a lane), double-buffered: the next tile streams in while the MFMAs read the
 //   current one, with no registers or VALU spent on staging and one barrier
-//   per tile.  Rows are XOR-swizzled by 16-byte chunk so an operand read of 32
-//   rows hits every bank group.
+//   per tile.  Rows are XOR-swizzled by 16-byte chunk, with a pattern per
+//   tile (K or V) chosen so the operand reads are free of bank conflicts.
 // * The sequence's block-table entries are staged in LDS once, so a K/V
 //   address never waits on a global load.
 // * The output is rescaled only when a tile's maximum score exceeds the
@@ -81,6 +81,25 @@ struct PrefillShape {
 template <int B>
 struct Buf {};
 
+// LDS position of 16-byte chunk c of a K or V row is c ^ swizzle(row).  The
+// swizzles are chosen per access pattern so that every 32 lanes the LDS serves
+// together hit distinct banks (64 banks of 4 bytes):
+// * K is read as 16-byte A operands, one row per lane, 32 consecutive rows:
+//   128-element rows use row mod 16; 64-element rows (two per bank line) use
+//   (row / 2) mod 8.
+// * V is read with ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive
+//   keys x 2 chunks x 2 halves, and the two groups of a half-wave differ in
+//   chunk bit 1; spreading the 4 keys over chunk bits 2-3 (D=128) or over
+//   chunk bit 2 and the bank-line half (D=64) separates all 32 lanes.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swizzle(int key) {
+  return D == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
@@ -95,9 +114,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     int64_t out_head_stride) {
   using S = PrefillShape<D, G>;
   // Two K/V tile buffers, row-major [key][dim], each row's 16-byte chunks
-  // XOR-swizzled by the row index: chunk c of row r sits at position
-  // c ^ (r mod kChunks), so reading one chunk column over 32 rows (an MFMA
-  // operand) touches every bank group instead of one.
+  // XOR-swizzled (k_swizzle / v_swizzle) so the MFMA operand reads are free
+  // of bank conflicts.
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
@@ -161,13 +179,13 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // Keys past wg_last_pos are in the future of every row of the tile and get
   // masked; they are fetched from position wg_last_pos (a readable row), so
   // P.V only ever multiplies finite values.
-  auto dma = [&](const uint16_t* cache, uint16_t* lds, int kt0) {
+  auto dma = [&](const uint16_t* cache, uint16_t* lds, int kt0, bool is_v) {
 #pragma unroll
     for (int i = 0; i < S::kDmaPerWave; ++i) {
       const int piece = wave * S::kDmaPerWave + i;
       const int row = piece * S::kRowsPerDma + lane / S::kChunks;
       const int pos = lane % S::kChunks;
-      const int chunk = pos ^ (row & (S::kChunks - 1));
+      const int chunk = pos ^ (is_v ? v_swizzle<D>(row) : k_swizzle<D>(row));
       const uint16_t* src = row_ptr(cache, min(kt0 + row, wg_last_pos)) + 8 * chunk;
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds + piece * 512), 16, 0,
                                        0);
@@ -179,7 +197,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   int k_off[S::kSteps];
 #pragma unroll
   for (int s = 0; s < S::kSteps; ++s)
-    k_off[s] = col * D + 8 * ((2 * s + half) ^ (col & (S::kChunks - 1)));
+    k_off[s] = col * D + 8 * ((2 * s + half) ^ k_swizzle<D>(col));  // rows col and col + 32
   // V operand (A of O^T = V^T P^T) via transpose reads: for read t of step ks,
   // lane (half, col) supplies the row of key ks*16 + 8t + 4 half + (col % 16) / 4
   // and dims db*32 + 16 (col / 16) + 4 (col % 4) .. +3; the read hands it the
@@ -192,7 +210,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
       const int key = 8 * t + 4 * half + (col % 16) / 4;
       const int j4 = col % 4;
       const int chunk = db * 4 + 2 * (col / 16) + j4 / 2;
-      v_off[t][db] = key * D + 8 * (chunk ^ (key & (S::kChunks - 1))) + 4 * (j4 % 2);
+      v_off[t][db] = key * D + 8 * (chunk ^ v_swizzle<D>(key)) + 4 * (j4 % 2);
     }
 
   f32x16_t acc_o[S::kDB];
@@ -300,16 +318,16 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     uint16_t* v_nxt = kFirst ? v_lds1 : v_lds0;
     const int kt0 = kt * kBN;
     if (kt + 1 < n_kt) {
-      dma(k_cache, k_nxt, kt0 + kBN);
-      dma(v_cache, v_nxt, kt0 + kBN);
+      dma(k_cache, k_nxt, kt0 + kBN, false);
+      dma(v_cache, v_nxt, kt0 + kBN, true);
     }
     if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0);  // else: all in this wave's future
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  dma(k_cache, k_lds0, 0);
-  dma(v_cache, v_lds0, 0);
+  dma(k_cache, k_lds0, 0, false);
+  dma(v_cache, v_lds0, 0, true);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
