@@ -168,27 +168,35 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
 
   const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;  // elements per slot
   const int bs_mask = (1 << bs_log2) - 1;
-  auto row_ptr = [&](const uint16_t* cache, int pos) {
-    const int64_t blk = bt_lds[pos >> bs_log2];
-    return cache + ((blk << bs_log2) + (pos & bs_mask)) * slot_stride + static_cast<int64_t>(g) * D;
-  };
 
   // A tile moves from HBM to LDS by DMA (global_load_lds): a wave-wide
   // instruction writes 1 KB of LDS, lane l's 16 bytes at offset 16 l, so each
   // lane fetches the source chunk that the swizzle places at its position.
   // Keys past wg_last_pos are in the future of every row of the tile and get
   // masked; they are fetched from position wg_last_pos (a readable row), so
-  // P.V only ever multiplies finite values.
-  auto dma = [&](const uint16_t* cache, uint16_t* lds, int kt0, bool is_v) {
+  // P.V only ever multiplies finite values.  K and V of a tile come from the same rows, so each row's slot offset is
+  // computed once for both DMAs.  A lane's row within the tile and its source
+  // chunks are the same for every tile.
+  int dma_row[S::kDmaPerWave], dma_kchunk[S::kDmaPerWave], dma_vchunk[S::kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < S::kDmaPerWave; ++i) {
+    const int row = (wave * S::kDmaPerWave + i) * S::kRowsPerDma + lane / S::kChunks;
+    dma_row[i] = row;
+    dma_kchunk[i] = (lane % S::kChunks) ^ k_swizzle<D>(row);
+    dma_vchunk[i] = (lane % S::kChunks) ^ v_swizzle<D>(row);
+  }
+  auto dma_kv = [&](uint16_t* k_lds, uint16_t* v_lds, int kt0) {
 #pragma unroll
     for (int i = 0; i < S::kDmaPerWave; ++i) {
       const int piece = wave * S::kDmaPerWave + i;
-      const int row = piece * S::kRowsPerDma + lane / S::kChunks;
-      const int pos = lane % S::kChunks;
-      const int chunk = pos ^ (is_v ? v_swizzle<D>(row) : k_swizzle<D>(row));
-      const uint16_t* src = row_ptr(cache, min(kt0 + row, wg_last_pos)) + 8 * chunk;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds + piece * 512), 16, 0,
-                                       0);
+      const int pos = min(kt0 + dma_row[i], wg_last_pos);
+      const int64_t blk = bt_lds[pos >> bs_log2];
+      const int64_t off = ((blk << bs_log2) + (pos & bs_mask)) * slot_stride +
+                          static_cast<int64_t>(g) * D;
+      const uint16_t* ks = k_cache + off + 8 * dma_kchunk[i];
+      const uint16_t* vs = v_cache + off + 8 * dma_vchunk[i];
+      __builtin_amdgcn_global_load_lds(ks, (lds_void_t*)(k_lds + piece * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs, (lds_void_t*)(v_lds + piece * 512), 16, 0, 0);
     }
   };
 
@@ -317,17 +325,13 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     uint16_t* k_nxt = kFirst ? k_lds1 : k_lds0;
     uint16_t* v_nxt = kFirst ? v_lds1 : v_lds0;
     const int kt0 = kt * kBN;
-    if (kt + 1 < n_kt) {
-      dma(k_cache, k_nxt, kt0 + kBN, false);
-      dma(v_cache, v_nxt, kt0 + kBN, true);
-    }
+    if (kt + 1 < n_kt) dma_kv(k_nxt, v_nxt, kt0 + kBN);
     if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0);  // else: all in this wave's future
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  dma(k_cache, k_lds0, 0, false);
-  dma(v_cache, v_lds0, 0, true);
+  dma_kv(k_lds0, v_lds0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < n_kt; kt += 2) {
