@@ -53,12 +53,64 @@ WORKLOAD_TEXT = {
 
 
 def decode_partition(case, cus=256):
-    """Split size: enough (sequence, kv head, split) waves to give every CU several."""
+    """Split size.  When sequences x kv heads already give every SIMD four waves,
+    one split per sequence.  Otherwise 512 tokens (long enough that the reduce is
+    cheap), halved until there is about one (sequence, kv head, split) wave per SIMD."""
     waves = case.num_seqs * case.num_kv_heads
-    p = 64
-    while p < 8192 and waves * math.ceil(case.max_context_len / (2 * p)) >= 4 * cus * 4:
-        p *= 2
+    if waves >= 16 * cus:
+        return 64 * max(1, math.ceil(case.max_context_len / 64))
+    p = 512
+    while p > 64 and waves * math.ceil(case.max_context_len / p) < 4 * cus:
+        p //= 2
     return p
+
+
+class HipEvents:
+    """Timing events from the HIP runtime torch already loaded, created with
+    hipEventDisableSystemFence: recording one then costs no system-scope cache
+    write-back, which otherwise puts microseconds between the kernels of a step.
+    They are recorded on the stream the library launches on."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, count):
+        import ctypes
+
+        import torch
+        torch.cuda.init()
+        self.ctypes = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.events.append(e)
+        self.stream = torch.cuda.current_stream()
+
+    def record(self, i):
+        rc = self.hip.hipEventRecord(self.events[i], self.ctypes.c_void_p(self.stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, i, j):
+        """Milliseconds from event i to event j (after a device synchronize)."""
+        f = self.ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ctypes.byref(f), self.events[i], self.events[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def __del__(self):
+        for e in getattr(self, "events", []):
+            self.hip.hipEventDestroy(e)
 
 
 class Runner:
@@ -90,40 +142,41 @@ class Runner:
     def flush(self):
         self.flush_sink.copy_(self.flush_buf.sum())
 
-    def step(self, ev):
+    def step(self, ev, k):
+        """One step; events 4k .. 4k+3 bracket store, main kernel and (decode) reduce."""
         pa, v, c = self.pa, self.vals, self.case
-        ev[0].record()
+        ev.record(4 * k)
         pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"], v["slot_mapping"])
-        ev[1].record()
+        ev.record(4 * k + 1)
         if self.kind == "decode":
             pa.pa_decode(v["q"], v["k_cache"], v["v_cache"], v["block_table"], v["context_lens"],
                          c.max_context_len, self.partition, c.scale, self.ws)
-            ev[2].record()
+            ev.record(4 * k + 2)
             pa.pa_decode_reduce(self.ws, v["context_lens"], self.splits, self.partition,
                                 self.out)
         else:
             pa.pa_prefill_varlen(v["q"], v["k_cache"], v["v_cache"], v["cu_seqlens_q"],
                                  v["cu_seqlens_k"], v["block_table"], c.max_seqlen_q,
                                  c.max_context_len, c.scale, self.out)
-            ev[2].record()
-        ev[3].record()
+            ev.record(4 * k + 2)
+        ev.record(4 * k + 3)
 
     def run(self, steps, warmup):
         torch = self.torch
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-        for _ in range(warmup):
+        ev = HipEvents(4 * max(steps, warmup))
+        for i in range(warmup):
             self.flush()
-            self.step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+            self.step(ev, i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             self.flush()
-            self.step(evs[i])
+            self.step(ev, i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        step_ms = [e[0].elapsed_time(e[3]) for e in evs]
-        store_ms = [e[0].elapsed_time(e[1]) for e in evs]
-        main_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        step_ms = [ev.ms(4 * i, 4 * i + 3) for i in range(steps)]
+        store_ms = [ev.ms(4 * i, 4 * i + 1) for i in range(steps)]
+        main_ms = [ev.ms(4 * i + 1, 4 * i + 2) for i in range(steps)]
         return dict(step_ms=sum(step_ms) / steps, store_ms=sum(store_ms) / steps,
                     main_ms=sum(main_ms) / steps, min_step_ms=min(step_ms),
                     wall_ms_per_step=1e3 * wall / steps)

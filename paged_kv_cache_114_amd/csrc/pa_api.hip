@@ -118,7 +118,8 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
   const size_t acc_elems = static_cast<size_t>(num_seqs) * num_q_heads * splits * head_dim;
   pa::DecodeArgs a{q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
                    block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
-                   head_dim, block_size, partition_tokens, splits, scale, ws, ws + acc_elems,
+                   head_dim, block_size, max_context_len, partition_tokens, splits, scale, ws,
+                   ws + acc_elems,
                    dtype == PA_DTYPE_BF16};
   return launched(pa::launch_decode(a, stream));
 }

@@ -14,9 +14,10 @@
 // * A head row (head_dim elements) is spread over kR lanes, 16 bytes each, so
 //   one wave load covers 64 / kR tokens with fully used 16-byte lanes; the kR
 //   partial dot products are combined with DPP row operations (no LDS).
-// * A tile issues kU such loads for K and for V before any arithmetic, so a
-//   wave keeps kU * 2 * 1 KiB in flight; several waves per SIMD cover HBM
-//   latency without software double buffering.
+// * A tile is kU such loads for K and for V.  The loads of the next tile are
+//   issued before the current one is consumed (two register sets), so the
+//   kU * 2 KiB of the next tile are in flight while a wave computes, and the
+//   register budget still fits several waves per SIMD.
 // * The workgroup holds NW waves = NW consecutive kv heads of the same
 //   (sequence, split): together they read the contiguous part of each token's
 //   [num_kv_heads, head_dim] row, and they share one staged copy of the
@@ -38,7 +39,7 @@ struct DecodeShape {
   static constexpr int kE = Chunk<T>::kElems;  // elements per lane per load
   static constexpr int kR = D / kE;            // lanes per head row
   static constexpr int kTpl = kWave / kR;      // tokens per wave load
-  static constexpr int kU = G >= 4 ? 4 : 8;    // loads per tile, each for K and V
+  static constexpr int kU = G >= 4 ? 2 : 4;    // loads per tile, each for K and V
   static constexpr int kTile = kTpl * kU;      // tokens per tile
   static_assert(kR >= 1 && kR <= kWave && (kWave % kR) == 0, "row must fit a wave");
 };
@@ -50,41 +51,49 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     const T* __restrict__ q, int64_t q_seq_stride, int64_t q_head_stride,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int64_t bt_stride,
-    const int32_t* __restrict__ context_lens, int32_t num_kv_heads, int32_t bs_log2,
-    int32_t partition_tokens, int32_t num_splits, float scale_log2, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml) {
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_kv_heads,
+    int32_t bs_log2, int32_t bt_entries, int32_t partition_tokens, int32_t num_splits,
+    float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
   using S = DecodeShape<T, D, G>;
   constexpr int kE = S::kE, kR = S::kR, kTpl = S::kTpl, kU = S::kU, kTile = S::kTile;
   extern __shared__ int32_t bt_lds[];
 
-  const int split = blockIdx.x;
-  const int b = blockIdx.z;
+  // Workgroups are handed to the 8 XCDs round-robin in launch order, and a
+  // sequence's later splits are empty when its context is short.  Rotating
+  // the sequence index by the split spreads every split level over all XCDs,
+  // so no XCD (with its own L2 and fabric share) ends up with most of the
+  // full splits.
+  const int split = blockIdx.z;
+  const int b = (blockIdx.x + num_seqs - split % num_seqs) % num_seqs;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int g = blockIdx.y * NW + wave;
-
-  const int ctx = context_lens[b];
-  const int t0 = split * partition_tokens;
-  if (t0 >= ctx) return;  // empty split: nothing written, the reduce skips it
-  const int t1 = min(t0 + partition_tokens, ctx);
-
-  // Stage the block-table entries this split touches (shared by all waves).
-  const int first_blk = t0 >> bs_log2;
-  const int nblk = ((t1 - 1) >> bs_log2) - first_blk + 1;
-  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride + first_blk;
-  for (int i = threadIdx.x; i < nblk; i += NW * kWave) bt_lds[i] = bt_row[i];
-  __syncthreads();
-
   const int row = lane / kR;  // which token of a wave load
   const int col = lane % kR;  // which 16-byte chunk of the head row
   const int num_q_heads = num_kv_heads * G;
+  const int t0 = split * partition_tokens;
+
+  // The context length, the split's block-table window and the query are
+  // independent loads, issued together: the window is the most a split can
+  // touch, clipped to the bt_entries columns every table row has.
+  const int first_blk = t0 >> bs_log2;
+  const int win = min((partition_tokens >> bs_log2) + 2, bt_entries - first_blk);
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride + first_blk;
+  for (int i = threadIdx.x; i < win; i += NW * kWave) bt_lds[i] = bt_row[i];
+  uint4 q_raw[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+    q_raw[i] = load16(q + static_cast<int64_t>(b) * q_seq_stride +
+                      static_cast<int64_t>(g * G + i) * q_head_stride + col * kE);
+  const int ctx = context_lens[b];
+  if (t0 >= ctx) return;  // empty split (uniform over the workgroup): nothing written
+  const int t1 = min(t0 + partition_tokens, ctx);
+  __syncthreads();  // bt_lds ready
 
   float qf[G][kE];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const T* qp = q + static_cast<int64_t>(b) * q_seq_stride +
-                  static_cast<int64_t>(g * G + i) * q_head_stride + col * kE;
-    Chunk<T>::widen(load16(qp), qf[i]);
+    Chunk<T>::widen(q_raw[i], qf[i]);
 #pragma unroll
     for (int e = 0; e < kE; ++e) qf[i][e] *= scale_log2;
   }
@@ -103,22 +112,25 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
   const T* vbase = v_cache + static_cast<int64_t>(g) * D + col * kE;
   const int bs_mask = (1 << bs_log2) - 1;
 
-  for (int tb = t0; tb < t1; tb += kTile) {
-    uint4 kr[kU], vr[kU];
+  // Loads of tile n+1 are issued before tile n is consumed, so a wave never
+  // waits on HBM with nothing else queued.  Rows past t1 read row t1 - 1
+  // (cached, finite) and are masked in the scores; the prefetch is never
+  // skipped, which keeps the compiler's wait counts exact (a conditional load
+  // would make it wait for every outstanding load).
+  auto load_tile = [&](int tb, uint4 (&kr)[kU], uint4 (&vr)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int j = tb + u * kTpl + row;
-      if (j < t1) {
-        const int64_t blk = bt_lds[(j >> bs_log2) - first_blk];
-        const int64_t off = ((blk << bs_log2) + (j & bs_mask)) * slot_stride;
-        kr[u] = load16(kbase + off);
-        vr[u] = load16(vbase + off);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
+      const int j = min(tb + u * kTpl + row, t1 - 1);
+      const int64_t blk = bt_lds[(j >> bs_log2) - first_blk];
+      const int64_t off = ((blk << bs_log2) + (j & bs_mask)) * slot_stride;
+      kr[u] = load16(kbase + off);
+      vr[u] = load16(vbase + off);
     }
+    // keep the scheduler from sinking these loads into the consume that follows
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
+  auto consume = [&](int tb, const uint4 (&kr)[kU], const uint4 (&vr)[kU]) {
     float sc[kU][G];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -135,16 +147,15 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
       }
     }
 
-    float alpha[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       float mt = sc[0][i];
 #pragma unroll
       for (int u = 1; u < kU; ++u) mt = fmaxf(mt, sc[u][i]);
       mt = across_groups_max<kR>(mt);
-      // The tile's first token (tb < t1) is valid, so mt and m_new are finite.
+      // m_new is finite: the first tile consumed starts at t0 < t1.
       const float m_new = fmaxf(m[i], mt);
-      alpha[i] = fast_exp2(m[i] - m_new);
+      const float alpha = fast_exp2(m[i] - m_new);
       m[i] = m_new;
       float psum = 0.f;
 #pragma unroll
@@ -152,9 +163,9 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
         sc[u][i] = fast_exp2(sc[u][i] - m_new);
         psum += sc[u][i];
       }
-      l[i] = l[i] * alpha[i] + psum;
+      l[i] = l[i] * alpha + psum;
 #pragma unroll
-      for (int e = 0; e < kE; ++e) acc[i][e] *= alpha[i];
+      for (int e = 0; e < kE; ++e) acc[i][e] *= alpha;
     }
 
 #pragma unroll
@@ -166,7 +177,24 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
 #pragma unroll
         for (int e = 0; e < kE; ++e) acc[i][e] = fmaf(sc[u][i], vf[e], acc[i][e]);
     }
-  }
+  };
+
+  // Two register sets alternate; the loop is unrolled by two by hand so no
+  // set is ever copied.  The body has no exit between a load and the consume
+  // that precedes its use (an early exit there lets the compiler sink the load
+  // to the next iteration, which removes the overlap).  When the split has an
+  // odd number of tiles the last consume sees a tile wholly past t1: every
+  // score is -inf, so it adds nothing (m is finite by then).
+  uint4 ka[kU], va[kU], kb[kU], vb[kU];
+  load_tile(t0, ka, va);
+  int tb = t0;
+  do {
+    load_tile(tb + kTile, kb, vb);
+    consume(tb, ka, va);
+    load_tile(tb + 2 * kTile, ka, va);
+    consume(tb + kTile, kb, vb);
+    tb += 2 * kTile;
+  } while (tb < t1);
 
   // Combine the wave's token rows (all share the running maximum m).
 #pragma unroll
@@ -237,13 +265,15 @@ __global__ __launch_bounds__(4 * kWave) void decode_reduce_kernel(
 template <typename T, int D, int G, int NW>
 hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
-  const int max_blk = (a.partition_tokens + a.block_size - 1) / a.block_size + 1;
-  dim3 grid(a.num_splits, a.num_kv_heads / NW, a.num_seqs);
+  const int max_blk = (a.partition_tokens >> bs_log2) + 2;
+  const int bt_entries = (a.max_context_len + a.block_size - 1) >> bs_log2;
+  dim3 grid(a.num_seqs, a.num_kv_heads / NW, a.num_splits);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, NW>), grid, dim3(NW * kWave),
                      max_blk * sizeof(int32_t), stream, static_cast<const T*>(a.q),
                      a.q_seq_stride, a.q_head_stride, static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_table, a.block_table_stride,
-                     a.context_lens, a.num_kv_heads, bs_log2, a.partition_tokens, a.num_splits,
+                     a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, bt_entries,
+                     a.partition_tokens, a.num_splits,
                      a.scale * kLog2e, a.ws_acc, a.ws_ml);
   return hipGetLastError();
 }

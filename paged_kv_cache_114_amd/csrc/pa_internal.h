@@ -27,7 +27,7 @@ struct DecodeArgs {
   int64_t block_table_stride;
   const int32_t* context_lens;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
-  int32_t partition_tokens, num_splits;
+  int32_t max_context_len, partition_tokens, num_splits;
   float scale;
   float* ws_acc;  // [B, Hq, S, D]
   float* ws_ml;   // [B, Hq, S, 2]
