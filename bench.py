@@ -65,6 +65,27 @@ def decode_partition(case, cus=256):
     return p
 
 
+def prefill_split_keys(case, cus=256, wgs_per_cu=2):
+    """Keys per work item for long query tiles.  The prefill's workgroups take
+    (query tile, kv head) items from a longest-first list, which balances a
+    batch by itself once it has more items than workgroup slots; with fewer
+    (one long sequence), long tiles are cut into key ranges of about 1.5x the
+    mean key tiles per slot, so every slot gets work."""
+    group = case.num_q_heads // case.num_kv_heads
+    rows = 32 * (1 if group >= 4 else 4 // group)
+    tiles = []
+    for lq, lk in zip(case.q_lens, case.context_lens):
+        lq, lk = int(lq), int(lk)
+        for t in range(math.ceil(lq / rows)):
+            tiles.append((lk - lq + min(lq, (t + 1) * rows) - 1) // 64 + 1)
+    slots = cus * wgs_per_cu
+    if not tiles or len(tiles) * case.num_kv_heads >= slots:
+        return 0
+    mean = case.num_kv_heads * sum(tiles) / slots
+    keys = 64 * max(4, math.ceil(1.5 * mean))
+    return 0 if keys >= 64 * max(tiles) else keys
+
+
 class HipEvents:
     """Timing events from the HIP runtime torch already loaded, created with
     hipEventDisableSystemFence: recording one then costs no system-scope cache
@@ -116,7 +137,7 @@ class HipEvents:
 class Runner:
     """Buffers and launches for one workload; times each step with HIP events."""
 
-    def __init__(self, name, partition=None):
+    def __init__(self, name, partition=None, split_keys=None):
         import torch
 
         import paged_kv_cache_114_amd as pa
@@ -136,6 +157,11 @@ class Runner:
                                    device="cuda:0")
         else:
             self.out = torch.empty_like(self.vals["q"])
+            self.split_keys = prefill_split_keys(c) if split_keys is None else split_keys
+            nbytes, self.splits = pa.pa_prefill_workspace_size(
+                c.num_seqs, c.num_new_tokens, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                c.max_context_len, self.split_keys)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
         self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
         self.flush_sink = torch.zeros((), dtype=torch.float32, device="cuda:0")
 
@@ -157,7 +183,8 @@ class Runner:
         else:
             pa.pa_prefill_varlen(v["q"], v["k_cache"], v["v_cache"], v["cu_seqlens_q"],
                                  v["cu_seqlens_k"], v["block_table"], c.max_seqlen_q,
-                                 c.max_context_len, c.scale, self.out)
+                                 c.max_context_len, c.scale, self.out, self.ws,
+                                 split_keys=self.split_keys)
             ev.record(4 * k + 2)
         ev.record(4 * k + 3)
 
@@ -212,7 +239,8 @@ class Runner:
         return {"workload": c.name, "prefill_TFLOPs_kernel": round(tf, 2),
                 "frac_bf16_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                 "ms_per_step": round(t["step_ms"], 5), "prefill_kernel_ms": round(t["main_ms"], 5),
-                "gflop": round(flops / 1e9, 3)}
+                "gflop": round(flops / 1e9, 3), "split_keys": self.split_keys,
+                "num_splits": self.splits}
 
 
 KERNEL_SOURCES = {
@@ -297,7 +325,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="decode split size in tokens (default: chosen from the workload)")
+    ap.add_argument("--split-keys", type=int, default=None,
+                    help="prefill keys per workgroup for long query tiles (0: no split; "
+                         "default: chosen from the workload)")
     ap.add_argument("--no-also", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -325,7 +357,7 @@ def main():
                           "launches": args.steps}), flush=True)
         return
 
-    main_run = Runner(args.workload, args.partition)
+    main_run = Runner(args.workload, args.partition, args.split_keys)
     t = main_run.run(args.steps, args.warmup)
     summ = main_run.summary(t)
     c = main_run.case

@@ -162,6 +162,34 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
                      int64_t out_head_stride, int32_t dtype, hipStream_t stream);
 
 /*
+ * pa_prefill_workspace_size -- host-only helper for pa_prefill_varlen.
+ *
+ * The prefill runs as a fixed set of workgroups (one per resident slot) that
+ * take work items -- (sequence, kv head, query tile, key range) -- from a
+ * device-built list ordered largest first, so a batch with one long sequence
+ * still keeps every compute unit busy.  A query tile whose keys span
+ * more than split_keys positions is cut into key ranges of split_keys keys;
+ * the ranges' partial results (the flash-decoding split of [Intro §9.5]
+ * applied to prefill) meet in a merge pass.  With S = ceil(max_seqlen_k /
+ * split_keys) (S = 1 when split_keys is 0, the no-split setting) the
+ * workspace holds, in order and 256-byte aligned: the work-list counter
+ * (256 bytes), the work list ((ceil(total_q / R) + num_seqs) * S *
+ * num_kv_heads entries of 8 bytes, R = 32 * max(1, 4 / group) query rows per
+ * tile), and when S > 1
+ *
+ *   acc [S, total_q, num_q_heads, head_dim]   then
+ *   ml  [S, total_q, num_q_heads, 2]
+ *
+ * floats: acc is a range's un-normalised output, ml its (m, l) in base-2
+ * units as for decode.  The library rewrites all of it on every call, so it
+ * needs no initialisation; a workspace serves one call at a time.
+ * split_keys must be 0 or a positive multiple of 64.
+ */
+int pa_prefill_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen_k,
+                              int32_t split_keys, size_t* bytes, int32_t* num_splits);
+
+/*
  * pa_prefill_varlen -- variable-length causal prefill over the paged cache.
  *
  * Defined by [Intro §10.2, §11.2, §13.2, §13.3]: sequence b owns query rows
@@ -182,9 +210,16 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
  *                 Lk <= max_seqlen_k.
  *   block_table   int32 [num_seqs, >= ceil(max_seqlen_k / block_size)],
  *                 row stride block_table_stride.
- * scale must be positive.  Supported: dtype bf16 (head_dim 64 or 128) and
- * ceil(max_seqlen_k / block_size) <= 8192; PA_DTYPE_F32 returns
- * PA_ERR_UNSUPPORTED.
+ *   split_keys    keys per workgroup for long query tiles (0: never split, a
+ *                 positive multiple of 64 otherwise); splitting shortens the
+ *                 longest workgroup's key loop when one sequence dominates.
+ *   workspace     device buffer of at least the bytes pa_prefill_workspace_size
+ *                 gives for the same sizes and split_keys, 16-byte aligned;
+ *                 workspace_bytes is checked.
+ * scale must be positive.  Supported: dtype bf16 (head_dim 64 or 128),
+ * num_seqs <= 4096 and ceil(max_seqlen_k / block_size) <= 8192;
+ * PA_DTYPE_F32 returns PA_ERR_UNSUPPORTED.  Enqueues the work-list build, the
+ * tile kernel and, when S > 1, the merge.
  */
 int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                       const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
@@ -192,7 +227,8 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
                       int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, int64_t num_blocks, int32_t max_seqlen_q,
-                      int32_t max_seqlen_k, float scale, void* out, int64_t out_tok_stride,
+                      int32_t max_seqlen_k, float scale, int32_t split_keys, void* workspace,
+                      size_t workspace_bytes, void* out, int64_t out_tok_stride,
                       int64_t out_head_stride, int32_t dtype, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -32,6 +32,7 @@ EXPORTS = (
     "pa_decode_workspace_size",
     "pa_decode",
     "pa_decode_reduce",
+    "pa_prefill_workspace_size",
     "pa_prefill_varlen",
 )
 
@@ -63,9 +64,13 @@ def _load():
                               i32, i32, f32, vp, sz, i32, vp]
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp, sz, vp, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp]
+    lib.pa_prefill_workspace_size.restype = ctypes.c_int
+    lib.pa_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                              ctypes.POINTER(sz), ctypes.POINTER(i32)]
     lib.pa_prefill_varlen.restype = ctypes.c_int
     lib.pa_prefill_varlen.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
-                                      i32, i32, i64, i32, i32, f32, vp, i64, i64, i32, vp]
+                                      i32, i32, i64, i32, i32, f32, i32, vp, sz, vp, i64, i64,
+                                      i32, vp]
     return lib
 
 
@@ -155,13 +160,29 @@ def pa_decode_reduce(workspace, context_lens, num_splits, partition_tokens, out,
         _dtype_code(out), _stream(stream)))
 
 
+def pa_prefill_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                              max_seqlen_k, split_keys=0):
+    """Returns ``(bytes, num_splits)`` of the prefill workspace for ``split_keys``."""
+    nbytes = ctypes.c_size_t(0)
+    splits = ctypes.c_int32(0)
+    _check("pa_prefill_workspace_size", library().pa_prefill_workspace_size(
+        num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, max_seqlen_k, split_keys,
+        ctypes.byref(nbytes), ctypes.byref(splits)))
+    return nbytes.value, splits.value
+
+
 def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
-                      max_seqlen_q, max_seqlen_k, scale, out, stream=None) -> None:
-    """Causal varlen prefill: ``q, out [Tq, Hq, d]``; K/V read from the paged caches."""
+                      max_seqlen_q, max_seqlen_k, scale, out, workspace, split_keys=0,
+                      stream=None) -> None:
+    """Causal varlen prefill: ``q, out [Tq, Hq, d]``; K/V read from the paged caches.
+    ``workspace``: a device tensor of at least pa_prefill_workspace_size bytes for the
+    same sizes and ``split_keys`` (> 0 cuts long query tiles' key loops)."""
     nb, bs, hkv, d = k_cache.shape
     tq, hq, _ = q.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check("pa_prefill_varlen", library().pa_prefill_varlen(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
         _ptr(cu_seqlens_k), _ptr(block_table), block_table.stride(0), cu_seqlens_q.shape[0] - 1,
-        tq, hq, hkv, d, bs, nb, max_seqlen_q, max_seqlen_k, scale, _ptr(out), out.stride(0),
-        out.stride(1), _dtype_code(q), _stream(stream)))
+        tq, hq, hkv, d, bs, nb, max_seqlen_q, max_seqlen_k, scale, split_keys,
+        _ptr(workspace), ws_bytes, _ptr(out), out.stride(0), out.stride(1), _dtype_code(q),
+        _stream(stream)))

@@ -155,13 +155,56 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
   return launched(pa::launch_reduce(a, stream));
 }
 
+namespace {
+
+// Prefill workspace layout (bytes): [0, 256) ticket counter and work-list
+// length; the work list (int2 per item, capacity items); then, when tiles are
+// split, acc [S, total_q, Hq, D] and ml [S, total_q, Hq, 2] floats.
+struct PrefillLayout {
+  size_t items_off, acc_off, ml_off, bytes;
+};
+
+PrefillLayout prefill_layout(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t splits) {
+  auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  const int64_t rows = pa::prefill_rows_per_tile(num_q_heads / num_kv_heads);
+  const size_t capacity =
+      static_cast<size_t>((total_q + rows - 1) / rows + num_seqs) * splits * num_kv_heads;
+  PrefillLayout l;
+  l.items_off = 256;
+  l.acc_off = round256(l.items_off + capacity * 8);
+  const size_t slots = splits > 1 ? static_cast<size_t>(splits) * total_q * num_q_heads : 0;
+  l.ml_off = round256(l.acc_off + slots * head_dim * sizeof(float));
+  l.bytes = round256(l.ml_off + slots * 2 * sizeof(float));
+  return l;
+}
+
+}  // namespace
+
+int pa_prefill_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen_k,
+                              int32_t split_keys, size_t* bytes, int32_t* num_splits) {
+  if (!bytes || !num_splits) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_q < 0 || head_dim <= 0 || max_seqlen_k < 0 || split_keys < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID_ARG;
+  if (split_keys % 64 != 0) return PA_ERR_UNSUPPORTED;
+  const int32_t s = split_keys == 0 ? 1 : (max_seqlen_k + split_keys - 1) / split_keys;
+  *num_splits = s > 1 ? s : 1;
+  *bytes = prefill_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, *num_splits)
+               .bytes;
+  return PA_OK;
+}
+
 int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                       const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
                       const int32_t* cu_seqlens_k, const int32_t* block_table,
                       int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, int64_t num_blocks, int32_t max_seqlen_q,
-                      int32_t max_seqlen_k, float scale, void* out, int64_t out_tok_stride,
+                      int32_t max_seqlen_k, float scale, int32_t split_keys, void* workspace,
+                      size_t workspace_bytes, void* out, int64_t out_tok_stride,
                       int64_t out_head_stride, int32_t dtype, hipStream_t stream) {
   const int eb = elt_bytes(dtype);
   if (eb == 0) return PA_ERR_UNSUPPORTED;
@@ -180,22 +223,40 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
       block_table_stride < 0)
     return PA_ERR_INVALID_ARG;
   if (!(scale > 0.f)) return PA_ERR_INVALID_ARG;  // also rejects NaN
+  size_t need = 0;
+  int32_t splits = 1;
+  const int st = pa_prefill_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                           max_seqlen_k, split_keys, &need, &splits);
+  if (st != PA_OK) return st;
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  if (num_seqs > pa::kPrefillPlanMaxSeqs) return PA_ERR_UNSUPPORTED;
+  {  // work items hold the query tile and the key range in 16 bits each
+    const int64_t rows = pa::prefill_rows_per_tile(num_q_heads / num_kv_heads);
+    if ((max_seqlen_q + rows - 1) / rows > 65535 || splits > 32767) return PA_ERR_UNSUPPORTED;
+  }
   if (num_blocks > INT32_MAX / block_size) return PA_ERR_UNSUPPORTED;  // 32-bit slots
   // the sequence's block-table entries are staged in LDS next to two K/V tiles
   if ((max_seqlen_k + int64_t{block_size} - 1) / block_size > kPrefillMaxTableEntries)
     return PA_ERR_UNSUPPORTED;
-  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_table || !out)
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_table || !out ||
+      !workspace)
     return PA_ERR_INVALID_ARG;
-  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (q_tok_stride * eb) % 16 || (q_head_stride * eb) % 16 || (out_tok_stride * eb) % 16 ||
       (out_head_stride * eb) % 16)
     return PA_ERR_UNSUPPORTED;
+  const PrefillLayout lay =
+      prefill_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, splits);
   pa::PrefillArgs a{q, q_tok_stride, q_head_stride, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
                     block_table, block_table_stride, num_seqs, num_q_heads, num_kv_heads,
-                    head_dim, block_size, max_seqlen_q, max_seqlen_k, scale, out,
-                    out_tok_stride, out_head_stride};
+                    head_dim, block_size, max_seqlen_q, max_seqlen_k, total_q, scale,
+                    split_keys, splits, static_cast<uint32_t*>(workspace),
+                    reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.items_off),
+                    reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc_off),
+                    reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off),
+                    out, out_tok_stride, out_head_stride};
   return launched(pa::launch_prefill(a, stream));
 }
 

@@ -56,11 +56,23 @@ struct PrefillArgs {
   const int32_t* block_table;
   int64_t block_table_stride;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
-  int32_t max_seqlen_q, max_seqlen_k;
+  int32_t max_seqlen_q, max_seqlen_k, total_q;
   float scale;
+  int32_t split_keys, num_splits;  // num_splits == 1: no split, ws_acc / ws_ml unused
+  uint32_t* tickets;               // work-list counter and length
+  int2* items;                     // work list written by the plan kernel
+  float* ws_acc;                   // [S, total_q, Hq, D]
+  float* ws_ml;                    // [S, total_q, Hq, 2]
   void* out;
   int64_t out_tok_stride, out_head_stride;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// The prefill work list is built by one workgroup that holds a per-sequence
+// table in LDS, which bounds the batch.
+constexpr int kPrefillPlanMaxSeqs = 4096;
+
+// Query positions per prefill work item for a GQA group size.
+inline int prefill_rows_per_tile(int group) { return 32 * (group >= 4 ? 1 : 4 / group); }
 
 }  // namespace pa

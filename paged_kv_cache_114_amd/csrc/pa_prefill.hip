@@ -110,7 +110,9 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_table, int64_t bt_stride, int32_t num_kv_heads,
-    int32_t bs_log2, float scale_log2, uint16_t* __restrict__ out, int64_t out_tok_stride,
+    int32_t bs_log2, float scale_log2, int32_t split_tiles, uint32_t* __restrict__ tickets,
+    const int2* __restrict__ items, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    int32_t total_q, uint16_t* __restrict__ out, int64_t out_tok_stride,
     int64_t out_head_stride) {
   using S = PrefillShape<D, G>;
   // Two K/V tile buffers, row-major [key][dim], each row's 16-byte chunks
@@ -122,61 +124,16 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * D];
   extern __shared__ int32_t bt_lds[];  // this sequence's block-table entries
 
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  const int q_begin = cu_q[b];
-  const int lq = cu_q[b + 1] - q_begin;
-  const int lk = cu_k[b + 1] - cu_k[b];
-  const int n_qt = (lq + S::kBM - 1) / S::kBM;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.z);  // heaviest tiles first
-  if (qt < 0) return;
-  const int ctx0 = lk - lq;                                 // cached positions
-  const int wg_q0 = qt * S::kBM;                            // first query row of the tile
-  const int wg_last_pos = ctx0 + min(lq, wg_q0 + S::kBM) - 1;
-  const int n_kt = wg_last_pos / kBN + 1;
+  __shared__ int ticket_lds;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int half = lane / 32;
   const int col = lane % 32;
-  const int head = g * G + wave / S::kRB;
-  const int w_q0 = wg_q0 + (wave % S::kRB) * 32;            // first query row of the wave
-  const int my_row = w_q0 + col;                            // this lane's query row
-  const bool row_ok = my_row < lq;
-  const int my_pos = ctx0 + my_row;                         // its position in the sequence
-  const int w_last_pos = ctx0 + min(lq - 1, w_q0 + 31);     // last position the wave needs
 
-  // Only keys 0..wg_last_pos are ever loaded, so the entries of blocks
-  // 0..wg_last_pos / block_size are all the tile needs.
-  {  // the block-table entries the tile's keys use, staged once
-    const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride;
-    const int n_bt = (wg_last_pos >> bs_log2) + 1;
-    for (int i = tid; i < n_bt; i += S::kThreads) bt_lds[i] = bt_row[i];
-  }
-
-  // Q^T fragments: lane (half, col) holds dims s*16 + 8*half .. +7 of query row col.
-  bf16x8_t qf[S::kSteps];
-  {
-    const uint16_t* qp = q + static_cast<int64_t>(q_begin + my_row) * q_tok_stride +
-                         static_cast<int64_t>(head) * q_head_stride + 8 * half;
-#pragma unroll
-    for (int s = 0; s < S::kSteps; ++s)
-      qf[s] = as_bf16x8(row_ok ? load16(qp + 16 * s) : make_uint4(0, 0, 0, 0));
-  }
-  __syncthreads();  // bt_lds ready
-
-  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;  // elements per slot
-  const int bs_mask = (1 << bs_log2) - 1;
-
-  // A tile moves from HBM to LDS by DMA (global_load_lds): a wave-wide
-  // instruction writes 1 KB of LDS, lane l's 16 bytes at offset 16 l, so each
-  // lane fetches the source chunk that the swizzle places at its position.
-  // Keys past wg_last_pos are in the future of every row of the tile and get
-  // masked; they are fetched from position wg_last_pos (a readable row), so
-  // P.V only ever multiplies finite values.  K and V of a tile come from the same rows, so each row's slot offset is
-  // computed once for both DMAs.  A lane's row within the tile and its source
-  // chunks are the same for every tile.
+  // This lane's DMA rows and source chunks, and its LDS offsets of the MFMA
+  // operands: fixed for the kernel.
   int dma_row[S::kDmaPerWave], dma_kchunk[S::kDmaPerWave], dma_vchunk[S::kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < S::kDmaPerWave; ++i) {
@@ -185,22 +142,6 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     dma_kchunk[i] = (lane % S::kChunks) ^ k_swizzle<D>(row);
     dma_vchunk[i] = (lane % S::kChunks) ^ v_swizzle<D>(row);
   }
-  auto dma_kv = [&](uint16_t* k_lds, uint16_t* v_lds, int kt0) {
-#pragma unroll
-    for (int i = 0; i < S::kDmaPerWave; ++i) {
-      const int piece = wave * S::kDmaPerWave + i;
-      const int pos = min(kt0 + dma_row[i], wg_last_pos);
-      const int64_t blk = bt_lds[pos >> bs_log2];
-      const int64_t off = ((blk << bs_log2) + (pos & bs_mask)) * slot_stride +
-                          static_cast<int64_t>(g) * D;
-      const uint16_t* ks = k_cache + off + 8 * dma_kchunk[i];
-      const uint16_t* vs = v_cache + off + 8 * dma_vchunk[i];
-      __builtin_amdgcn_global_load_lds(ks, (lds_void_t*)(k_lds + piece * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs, (lds_void_t*)(v_lds + piece * 512), 16, 0, 0);
-    }
-  };
-
-  // Per-lane LDS offsets (elements) of the MFMA operands, fixed for the kernel.
   // K operand (A of S^T = K Q^T): row mb*32 + col, chunk 2s + half.
   int k_off[S::kSteps];
 #pragma unroll
@@ -220,6 +161,92 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
       const int chunk = db * 4 + 2 * (col / 16) + j4 / 2;
       v_off[t][db] = key * D + 8 * (chunk ^ v_swizzle<D>(key)) + 4 * (j4 % 2);
     }
+  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;  // elements per slot
+  const int bs_mask = (1 << bs_log2) - 1;
+
+  // Work entries come from the plan heaviest first, the kv heads of one query
+  // tile side by side (they read the same K/V rows, so those DRAM pages are
+  // open together).  A workgroup's first entry is its own index; after that
+  // it takes the next one from a counter as soon as it is free, claimed while
+  // it works on its last key tile so the claim's latency is hidden.  The long
+  // key loops start first and the short ones fill the gaps around them.
+  const int n_entries = static_cast<int>(tickets[1]);
+  int next_entry = blockIdx.x;  // meaningful in thread 0 only
+  for (;;) {
+  if (tid == 0) ticket_lds = next_entry;
+  __syncthreads();
+  const int entry = ticket_lds;
+  if (entry >= n_entries) break;  // uniform: every wave leaves together
+  const int2 item = items[entry];
+  const int b = item.x & 0xffff;
+  const int g = item.x >> 16;
+  const int qt = item.y & 0xffff;
+  const int split = item.y >> 16;
+  const int q_begin = cu_q[b];
+  const int lq = cu_q[b + 1] - q_begin;
+  const int lk = cu_k[b + 1] - cu_k[b];
+  const int ctx0 = lk - lq;                                 // cached positions
+  const int wg_q0 = qt * S::kBM;                            // first query row of the tile
+  const int wg_last_pos = ctx0 + min(lq, wg_q0 + S::kBM) - 1;
+  const int n_kt = wg_last_pos / kBN + 1;
+  // A tile that needs more than split_tiles key tiles is cut into key ranges
+  // of split_tiles tiles, one item each; their partial results meet in the
+  // merge kernel.  Split 0 always holds key 0, which every row sees.
+  const int n_split = (n_kt + split_tiles - 1) / split_tiles;
+  const int kt_begin = split * split_tiles;
+  const int kt_end = min(n_kt, kt_begin + split_tiles);
+  const int last_pos = min(kt_end * kBN - 1, wg_last_pos);  // last key this item loads
+
+  const int head = g * G + wave / S::kRB;
+  const int w_q0 = wg_q0 + (wave % S::kRB) * 32;            // first query row of the wave
+  const int my_row = w_q0 + col;                            // this lane's query row
+  const bool row_ok = my_row < lq;
+  const int my_pos = ctx0 + my_row;                         // its position in the sequence
+  const int w_last_pos = ctx0 + min(lq - 1, w_q0 + 31);     // last position the wave needs
+
+  // Only keys kt_begin * 64 .. last_pos are ever loaded, so the entries of
+  // their blocks are all the workgroup needs.
+  const int first_blk = (kt_begin * kBN) >> bs_log2;
+  {  // the block-table entries the tile's keys use, staged once
+    const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride + first_blk;
+    const int n_bt = (last_pos >> bs_log2) - first_blk + 1;
+    for (int i = tid; i < n_bt; i += S::kThreads) bt_lds[i] = bt_row[i];
+  }
+
+  // Q^T fragments: lane (half, col) holds dims s*16 + 8*half .. +7 of query row col.
+  bf16x8_t qf[S::kSteps];
+  {
+    const uint16_t* qp = q + static_cast<int64_t>(q_begin + my_row) * q_tok_stride +
+                         static_cast<int64_t>(head) * q_head_stride + 8 * half;
+#pragma unroll
+    for (int s = 0; s < S::kSteps; ++s)
+      qf[s] = as_bf16x8(row_ok ? load16(qp + 16 * s) : make_uint4(0, 0, 0, 0));
+  }
+  __syncthreads();  // bt_lds ready
+
+  // A tile moves from HBM to LDS by DMA (global_load_lds): a wave-wide
+  // instruction writes 1 KB of LDS, lane l's 16 bytes at offset 16 l, so each
+  // lane fetches the source chunk that the swizzle places at its position.
+  // Keys past last_pos are masked (past wg_last_pos they are in the future of
+  // every row) or belong to the next split; they are fetched from position
+  // last_pos (a readable row), so
+  // P.V only ever multiplies finite values.  K and V of a tile come from the same rows, so each row's slot offset is
+  // computed once for both DMAs.  A lane's row within the tile and its source
+  // chunks are the same for every tile.
+  auto dma_kv = [&](uint16_t* k_lds, uint16_t* v_lds, int kt0) {
+#pragma unroll
+    for (int i = 0; i < S::kDmaPerWave; ++i) {
+      const int piece = wave * S::kDmaPerWave + i;
+      const int pos = min(kt0 + dma_row[i], last_pos);
+      const int64_t blk = bt_lds[(pos >> bs_log2) - first_blk];
+      const int64_t off = ((blk << bs_log2) + (pos & bs_mask)) * slot_stride +
+                          static_cast<int64_t>(g) * D;
+      const uint16_t* ks = k_cache + off + 8 * dma_kchunk[i];
+      const uint16_t* vs = v_cache + off + 8 * dma_vchunk[i];
+      __builtin_amdgcn_global_load_lds(ks, (lds_void_t*)(k_lds + piece * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs, (lds_void_t*)(v_lds + piece * 512), 16, 0, 0);
+    }
+  };
 
   f32x16_t acc_o[S::kDB];
 #pragma unroll
@@ -260,13 +287,17 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;  // scale_log2 > 0
     if (__ballot(tmax > m_ref + kLazy)) {  // wave-uniform: raise the reference
       const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      // a row that has seen no key yet (m_ref = m_new = -inf) keeps alpha = 1
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < S::kDB; ++db) acc_o[db] *= alpha;
     }
 
+    // A row of a later split may not have seen a key yet (m_ref = -inf, every
+    // score -inf): take its p against 0, which gives 0, instead of NaN.
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     // p = 2^(t - m_ref) as a bf16 head (truncated) plus a bf16 remainder,
     // packed two per word in the order the B operand of P.V wants
     float psum = 0.f;
@@ -275,8 +306,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -m_ref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r + 1], scale_log2, -m_ref));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r + 1], scale_log2, -m_use));
         psum += p0 + p1;
         const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
         const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
@@ -325,22 +356,38 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     uint16_t* k_nxt = kFirst ? k_lds1 : k_lds0;
     uint16_t* v_nxt = kFirst ? v_lds1 : v_lds0;
     const int kt0 = kt * kBN;
-    if (kt + 1 < n_kt) dma_kv(k_nxt, v_nxt, kt0 + kBN);
+    if (tid == 0 && kt + 1 == kt_end)
+      next_entry = static_cast<int>(gridDim.x + atomicAdd(tickets, 1u));
+    if (kt + 1 < kt_end) dma_kv(k_nxt, v_nxt, kt0 + kBN);
     if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0);  // else: all in this wave's future
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  dma_kv(k_lds0, v_lds0, 0);
+  dma_kv(k_lds0, v_lds0, kt_begin * kBN);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; kt += 2) {
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
     iteration(kt, Buf<0>{});
-    if (kt + 1 < n_kt) iteration(kt + 1, Buf<1>{});
+    if (kt + 1 < kt_end) iteration(kt + 1, Buf<1>{});
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  if (!row_ok) return;
+  if (row_ok && n_split > 1) {
+    // Partial result of this key range, against its own reference maximum:
+    // acc [split][row][head][D] un-normalised, ml [split][row][head] = (m, l).
+    const int64_t slot =
+        (static_cast<int64_t>(split) * total_q + q_begin + my_row) * (num_kv_heads * G) + head;
+    float* pp = ws_acc + slot * D;
+#pragma unroll
+    for (int db = 0; db < S::kDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(pp + db * 32 + 8 * r4 + 4 * half) =
+            make_float4(acc_o[db][4 * r4], acc_o[db][4 * r4 + 1], acc_o[db][4 * r4 + 2],
+                        acc_o[db][4 * r4 + 3]);
+    if (half == 0) reinterpret_cast<float2*>(ws_ml)[slot] = make_float2(m_ref, l_tot);
+  } else if (row_ok) {
   const float inv = 1.f / l_tot;
   uint16_t* op = out + static_cast<int64_t>(q_begin + my_row) * out_tok_stride +
                  static_cast<int64_t>(head) * out_head_stride;
@@ -355,6 +402,188 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
                           (static_cast<uint32_t>(f32_to_bf16_rne(acc_o[db][4 * r4 + 3] * inv)) << 16);
       *reinterpret_cast<uint2*>(op + dim) = make_uint2(lo, hi);
     }
+  }
+  }  // next item
+}
+
+// Work list of the prefill kernel, built on the device by one workgroup: one
+// entry per (sequence, query tile, key range, kv head), ordered by the number
+// of key tiles the entry covers, largest first (a counting sort; the order
+// among equal weights is arbitrary and does not change any result), the kv
+// heads of one (tile, range) adjacent.  tickets[0] is the claim counter, reset
+// here; tickets[1] the number of entries.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 1024;  // weights >= kPlanBins - 1 share the last bin
+
+template <int BM>
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
+    int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
+    int2* __restrict__ items) {
+  __shared__ int tile_start[kPrefillPlanMaxSeqs + 1];  // first query-tile index per sequence
+  __shared__ int seq_lq[kPrefillPlanMaxSeqs];
+  __shared__ int seq_ctx0[kPrefillPlanMaxSeqs];
+  __shared__ int bin_count[kPlanBins];
+  __shared__ int bin_base[kPlanBins];
+  __shared__ int scan[kPlanThreads];
+  const int tid = threadIdx.x;
+  bin_count[tid] = 0;
+  static_assert(kPlanBins == kPlanThreads, "one bin per thread");
+
+  // Inclusive block scan of scan[] (Hillis-Steele; kPlanThreads entries).
+  auto block_scan = [&]() {
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+  };
+
+  // 1. per sequence: query rows, cached positions, query tiles and the
+  //    exclusive prefix of the tile counts; each thread owns kPer consecutive
+  //    sequences
+  constexpr int kPer = (kPrefillPlanMaxSeqs + kPlanThreads - 1) / kPlanThreads;
+  int n_local[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = tid * kPer + k;
+    n_local[k] = 0;
+    if (b < num_seqs) {
+      const int lq = cu_q[b + 1] - cu_q[b];
+      seq_lq[b] = lq;
+      seq_ctx0[b] = cu_k[b + 1] - cu_k[b] - lq;
+      n_local[k] = (lq + BM - 1) / BM;
+    }
+    sum += n_local[k];
+  }
+  scan[tid] = sum;
+  __syncthreads();
+  block_scan();
+  int run = scan[tid] - sum;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = tid * kPer + k;
+    if (b < num_seqs) tile_start[b] = run;
+    run += n_local[k];
+  }
+  if (tid == kPlanThreads - 1) tile_start[num_seqs] = scan[tid];
+  __syncthreads();
+  const int n_tiles = tile_start[num_seqs];
+
+  // Visit every (tile, range): tile i belongs to the last sequence whose first
+  // tile is at or before i (sequences without tiles share their successor's
+  // start).
+  auto for_each_range = [&](auto&& fn) {
+    for (int i = tid; i < n_tiles; i += kPlanThreads) {
+      int lo = 0, hi = num_seqs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (tile_start[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      const int b = lo;
+      const int qt = i - tile_start[b];
+      const int n_kt = (seq_ctx0[b] + min(seq_lq[b], (qt + 1) * BM) - 1) / kBN + 1;
+      const int n_split = (n_kt + split_tiles - 1) / split_tiles;
+      for (int sp = 0; sp < n_split; ++sp)
+        fn(b, qt, sp, min(min(split_tiles, n_kt - sp * split_tiles), kPlanBins - 1));
+    }
+  };
+
+  // 2. ranges per weight
+  for_each_range([&](int, int, int, int w) { atomicAdd(&bin_count[w], 1); });
+  __syncthreads();
+  // 3. bin bases for descending weight order, in entries
+  const int c = bin_count[kPlanBins - 1 - tid] * num_kv_heads;
+  scan[tid] = c;
+  __syncthreads();
+  block_scan();
+  bin_base[kPlanBins - 1 - tid] = scan[tid] - c;
+  const int n_entries = scan[kPlanThreads - 1];
+  __syncthreads();
+  bin_count[tid] = 0;
+  __syncthreads();
+  // 4. placement: the kv heads of a range take consecutive entries
+  for_each_range([&](int b, int qt, int sp, int w) {
+    const int at = bin_base[w] + atomicAdd(&bin_count[w], num_kv_heads);
+    for (int g = 0; g < num_kv_heads; ++g)
+      items[at + g] = make_int2(b | (g << 16), qt | (sp << 16));
+  });
+  if (tid == 0) {
+    tickets[0] = 0u;
+    tickets[1] = static_cast<uint32_t>(n_entries);
+  }
+}
+
+// Merge of the key-range partials of split query tiles ([Intro §9.5]: each
+// partial carries its own maximum m_s and sum l_s, so the output is
+// sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s with m* = max_s m_s).
+// A query tile's (row, query head, 4 dims) items are spread over
+// kMergeParts workgroups, one item per thread, so the many short dependent
+// loads of a merge overlap across waves; consecutive threads take
+// consecutive dims, so each partial row is read with coalesced 16-byte loads.
+template <int D, int G>
+struct MergeShape {
+  static constexpr int kChunks = D / 4;                                  // items per (row, head)
+  static constexpr int kItems = PrefillShape<D, G>::kBM * G * kChunks;  // per query tile
+  static constexpr int kParts = kItems / 256;
+  static_assert(kItems % 256 == 0, "a tile's items fill whole workgroups");
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_kv_heads,
+    int32_t split_tiles, const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
+    int32_t total_q, uint16_t* __restrict__ out, int64_t out_tok_stride,
+    int64_t out_head_stride) {
+  using S = PrefillShape<D, G>;
+  using M = MergeShape<D, G>;
+  const int g = blockIdx.x / M::kParts;
+  const int item = (blockIdx.x % M::kParts) * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  const int q_begin = cu_q[b];
+  const int lq = cu_q[b + 1] - q_begin;
+  const int lk = cu_k[b + 1] - cu_k[b];
+  const int n_qt = (lq + S::kBM - 1) / S::kBM;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.z);
+  if (qt < 0) return;
+  const int wg_q0 = qt * S::kBM;
+  const int wg_last_pos = lk - lq + min(lq, wg_q0 + S::kBM) - 1;
+  const int n_split = (wg_last_pos / kBN + split_tiles) / split_tiles;
+  if (n_split <= 1) return;  // written directly by the prefill kernel
+  const int c = item % M::kChunks;
+  const int i = (item / M::kChunks) % G;
+  const int r = item / (M::kChunks * G);
+  if (wg_q0 + r >= lq) return;
+  const int64_t row = q_begin + wg_q0 + r;
+  const int64_t head = g * G + i;
+  const int64_t num_q_heads = static_cast<int64_t>(num_kv_heads) * G;
+  const int64_t split_stride = static_cast<int64_t>(total_q) * num_q_heads;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + row * num_q_heads + head;
+  const float* acc = ws_acc + (row * num_q_heads + head) * D + 4 * c;
+  // split 0 holds key 0, which every row sees, so m_star is finite
+  float m_star = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) m_star = fmaxf(m_star, ml[sp * split_stride].x);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float2 st = ml[sp * split_stride];
+    const float4 v = *reinterpret_cast<const float4*>(acc + sp * split_stride * D);
+    const float w = st.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.x - m_star);
+    l = fmaf(w, st.y, l);
+    o.x = fmaf(w, v.x, o.x);
+    o.y = fmaf(w, v.y, o.y);
+    o.z = fmaf(w, v.z, o.z);
+    o.w = fmaf(w, v.w, o.w);
+  }
+  const float inv = 1.f / l;
+  const uint32_t lo = f32_to_bf16_rne(o.x * inv) |
+                      (static_cast<uint32_t>(f32_to_bf16_rne(o.y * inv)) << 16);
+  const uint32_t hi = f32_to_bf16_rne(o.z * inv) |
+                      (static_cast<uint32_t>(f32_to_bf16_rne(o.w * inv)) << 16);
+  *reinterpret_cast<uint2*>(out + row * out_tok_stride + head * out_head_stride + 4 * c) =
+      make_uint2(lo, hi);
 }
 
 template <int D, int G>
@@ -363,12 +592,35 @@ hipError_t run(const PrefillArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
   const int tiles = (a.max_seqlen_q + S::kBM - 1) / S::kBM;
   const size_t bt_bytes = static_cast<size_t>((a.max_seqlen_k + a.block_size - 1) >> bs_log2) * 4;
-  dim3 grid(a.num_kv_heads, a.num_seqs, tiles);
-  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(S::kThreads), bt_bytes, stream,
+  // split_tiles >= every tile's key-tile count when nothing is split
+  const int split_tiles = a.num_splits > 1 ? a.split_keys / kBN : (a.max_seqlen_k + kBN - 1) / kBN;
+  hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
+                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, split_tiles, a.num_kv_heads,
+                     a.tickets, a.items);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // one workgroup per resident slot: they stay until the work list is empty
+  int dev = 0, cus = 0, occ = 0;
+  if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+  if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return err;
+  if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<D, G>, S::kThreads,
+                                                          bt_bytes)) != hipSuccess)
+    return err;
+  occ = occ > 0 ? occ : 1;
+  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(cus * occ), dim3(S::kThreads), bt_bytes, stream,
                      static_cast<const uint16_t*>(a.q), a.q_tok_stride, a.q_head_stride,
                      static_cast<const uint16_t*>(a.k_cache), static_cast<const uint16_t*>(a.v_cache),
                      a.cu_seqlens_q, a.cu_seqlens_k, a.block_table, a.block_table_stride,
-                     a.num_kv_heads, bs_log2, a.scale * kLog2e, static_cast<uint16_t*>(a.out),
+                     a.num_kv_heads, bs_log2, a.scale * kLog2e, split_tiles, a.tickets, a.items,
+                     a.ws_acc, a.ws_ml, a.total_q, static_cast<uint16_t*>(a.out),
+                     a.out_tok_stride, a.out_head_stride);
+  err = hipGetLastError();
+  if (err != hipSuccess || a.num_splits == 1) return err;
+  hipLaunchKernelGGL((prefill_merge_kernel<D, G>),
+                     dim3(a.num_kv_heads * MergeShape<D, G>::kParts, a.num_seqs, tiles), dim3(256),
+                     0, stream, a.cu_seqlens_q, a.cu_seqlens_k, a.num_kv_heads, split_tiles,
+                     a.ws_acc, a.ws_ml, a.total_q, static_cast<uint16_t*>(a.out),
                      a.out_tok_stride, a.out_head_stride);
   return hipGetLastError();
 }

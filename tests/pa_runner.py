@@ -70,12 +70,25 @@ def run_decode(case, vals, partition_tokens, ws=None, out=None, splits=None, q=N
     return out, ws, splits
 
 
-def run_prefill(case, vals, out=None):
+def prefill_workspace(case, split_keys=0, total_q=None):
+    """Workspace for a prefill, NaN-filled so a read of a partial-result slot the
+    tile kernel did not write shows up in the output."""
+    total_q = case.num_new_tokens if total_q is None else total_q
+    nbytes, _ = pa.pa_prefill_workspace_size(case.num_seqs, total_q, case.num_q_heads,
+                                             case.num_kv_heads, case.head_dim,
+                                             case.max_context_len, split_keys)
+    return torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=DEV)
+
+
+def run_prefill(case, vals, out=None, split_keys=0, workspace=None):
     if out is None:
         out = torch.empty_like(vals["q"])
+    if workspace is None:
+        workspace = prefill_workspace(case, split_keys)
     pa.pa_prefill_varlen(vals["q"], vals["k_cache"], vals["v_cache"], vals["cu_seqlens_q"],
                          vals["cu_seqlens_k"], vals["block_table"], case.max_seqlen_q,
-                         case.max_context_len, case.scale, out)
+                         case.max_context_len, case.scale, out, workspace,
+                         split_keys=split_keys)
     return out
 
 

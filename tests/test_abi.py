@@ -135,13 +135,14 @@ def test_reduce_validation():
 def prefill(**kw):
     args = dict(q=NULL, qt=2048, qh=128, kc=NULL, vc=NULL, cq=NULL, ck=NULL, bt=NULL, bts=8, b=8,
                 tq=6000, hq=16, hkv=8, d=128, bs=256, nb=64, mq=2048, mk=2048, scale=0.088,
-                out=NULL, ot=2048, oh=128, dtype=BF16)
+                sk=0, ws=NULL, wsb=0, out=NULL, ot=2048, oh=128, dtype=BF16)
     args.update(kw)
     a = args
     return pa.library().pa_prefill_varlen(a["q"], a["qt"], a["qh"], a["kc"], a["vc"], a["cq"],
                                           a["ck"], a["bt"], a["bts"], a["b"], a["tq"], a["hq"],
                                           a["hkv"], a["d"], a["bs"], a["nb"], a["mq"], a["mk"],
-                                          a["scale"], a["out"], a["ot"], a["oh"], a["dtype"], NULL)
+                                          a["scale"], a["sk"], a["ws"], a["wsb"], a["out"],
+                                          a["ot"], a["oh"], a["dtype"], NULL)
 
 
 def test_prefill_validation():
@@ -156,3 +157,35 @@ def test_prefill_validation():
     assert prefill(scale=-0.5) == pa.PA_ERR_INVALID_ARG
     assert prefill(scale=float("nan")) == pa.PA_ERR_INVALID_ARG
     assert prefill(bs=8, mk=8 * 16384 + 1, mq=100) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_prefill_workspace_size_formula():
+    r256 = lambda x: (x + 255) // 256 * 256
+    # group 2: 64-row tiles; no split -> counter + work list only
+    nbytes, splits = pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 0)
+    assert splits == 1 and nbytes == r256(256 + ((6000 + 63) // 64 + 8) * 8 * 8)
+    assert pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 2048)[1] == 1
+    nbytes, splits = pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 768)
+    items = r256(256 + ((6000 + 63) // 64 + 8) * 3 * 8 * 8)
+    acc = r256(items + 3 * 6000 * 16 * 128 * 4)
+    assert splits == 3 and nbytes == r256(acc + 3 * 6000 * 16 * 2 * 4)
+    # group 8: 32-row tiles
+    nbytes, _ = pa.pa_prefill_workspace_size(2, 100, 16, 2, 64, 100, 0)
+    assert nbytes == r256(256 + (4 + 2) * 2 * 8)
+    for bad in (100, -64):
+        with pytest.raises(pa.PAError):
+            pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, bad)
+
+
+def test_prefill_split_validation():
+    fake = ctypes.c_void_p(256)
+    ptrs = dict(q=fake, kc=fake, vc=fake, cq=fake, ck=fake, bt=fake, out=fake)
+    big = 1 << 40
+    assert prefill(sk=100, ws=fake, wsb=big, **ptrs) == pa.PA_ERR_UNSUPPORTED  # not 64k
+    assert prefill(sk=-64, ws=fake, wsb=big, **ptrs) == pa.PA_ERR_INVALID_ARG
+    assert prefill(**ptrs) == pa.PA_ERR_INVALID_ARG                   # no workspace
+    assert prefill(sk=512, ws=fake, wsb=1000, **ptrs) == pa.PA_ERR_WORKSPACE
+    assert prefill(ws=ctypes.c_void_p(264), wsb=big, **ptrs) == pa.PA_ERR_UNSUPPORTED  # align
+    assert prefill(b=5000, ws=fake, wsb=big, **ptrs) == pa.PA_ERR_UNSUPPORTED    # > 4096 seqs
+    assert prefill(sk=64, bs=8, mk=8 * 65536, mq=8 * 8192, tq=8 * 8192, ws=fake, wsb=big,
+                   **ptrs) == pa.PA_ERR_UNSUPPORTED                  # > 32767 key ranges

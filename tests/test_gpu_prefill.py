@@ -7,21 +7,21 @@ import pytest
 import torch
 
 import workloads as W
-from pa_runner import (DEV, HostInputs, assert_close, decode_buffers, run_decode, run_prefill,
-                       run_store, to_f64)
+from pa_runner import (DEV, HostInputs, assert_close, decode_buffers, prefill_workspace,
+                       run_decode, run_prefill, run_store, to_f64)
 
 import paged_kv_cache_114_amd as pa
 
 pytestmark = pytest.mark.gpu
 
 
-def _prefill_vs_oracle(case, seqs=None):
+def _prefill_vs_oracle(case, seqs=None, split_keys=0):
     print(f"prefill case={case.name} B={case.num_seqs} Tq={case.num_new_tokens} "
-          f"max_k={case.max_context_len}", flush=True)
+          f"max_k={case.max_context_len} split_keys={split_keys}", flush=True)
     vals = W.materialize(case, DEV)
     host = HostInputs(case, vals, seqs)
     run_store(vals)
-    out = run_prefill(case, vals)
+    out = run_prefill(case, vals, split_keys=split_keys)
     torch.cuda.synchronize()
     ref = host.prefill()
     got = to_f64(out, case.dtype)[host.token_rows]
@@ -111,7 +111,9 @@ def test_prefill_page_causal_example():
     cu = torch.tensor([0, 3], dtype=torch.int32, device=DEV)
     bt = torch.tensor([[1]], dtype=torch.int32, device=DEV)
     out = torch.empty_like(q)
-    pa.pa_prefill_varlen(q, kc, kc, cu, cu, bt, 3, 3, 1 / math.sqrt(2.0), out)
+    nbytes, _ = pa.pa_prefill_workspace_size(1, 3, 2, 1, 64, 3)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    pa.pa_prefill_varlen(q, kc, kc, cu, cu, bt, 3, 3, 1 / math.sqrt(2.0), out, ws)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     want_rows = np.array([[1.0, 0.0], [0.3302, 0.6698], [0.7517, 0.7517]])
@@ -130,8 +132,65 @@ def test_prefill_padding_only_rows_untouched_outside_sequences():
                         device=DEV)
     big_q[:tq] = vals["q"]
     out = torch.full_like(big_q, 7.0)
+    ws = prefill_workspace(case, total_q=tq + 5)
     pa.pa_prefill_varlen(big_q, vals["k_cache"], vals["v_cache"], vals["cu_seqlens_q"],
                          vals["cu_seqlens_k"], vals["block_table"], case.max_seqlen_q,
-                         case.max_context_len, case.scale, out)
+                         case.max_context_len, case.scale, out, ws)
     torch.cuda.synchronize()
     assert torch.all(out[tq:] == 7.0)
+
+
+# ------------------------------------------------------------------ split key ranges
+
+def test_prefill_split_c3_full_all_sequences():
+    """The Qwen3-0.6B varlen batch with long query tiles cut into 768-key ranges."""
+    _prefill_vs_oracle(W.c3_prefill(), split_keys=768)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,split_keys", [
+    (16, 8, 128, 256, 64),    # every key tile its own range
+    (16, 8, 128, 16, 128),
+    (8, 8, 128, 64, 192),     # group 1 (128-row tiles)
+    (16, 2, 128, 32, 64),     # group 8
+    (16, 8, 64, 128, 64),     # head_dim 64
+])
+def test_prefill_split_shapes_and_ragged_edges(hq, hkv, d, bs, split_keys):
+    # ranges that start inside a tile's diagonal leave early rows with no visible key
+    lengths = [1, 5, 64, 65, 130, 300, 700, 257]
+    cached = [0, 0, 0, 1, 64, 100, 256, 256]
+    case = W.prefill_case(f"psplit_{hq}_{hkv}_{d}_{bs}_{split_keys}", 900 + hq + d + bs,
+                          lengths=lengths, cached=cached, hq=hq, hkv=hkv, d=d, bs=bs)
+    _prefill_vs_oracle(case, split_keys=split_keys)
+
+
+def test_prefill_split_leaves_short_tiles_bit_identical():
+    """Tiles with no more key tiles than a range are computed exactly as without
+    splitting; only the long tiles go through the merge."""
+    case = W.prefill_case("splitsame", 617, lengths=[900, 356], cached=[0, 256])
+    vals = W.materialize(case, DEV)
+    run_store(vals)
+    plain = run_prefill(case, vals)
+    split = run_prefill(case, vals, split_keys=256)
+    torch.cuda.synchronize()
+    # sequence 0: rows 0..255 need at most 4 key tiles (64-row tiles); sequence 1: all
+    # 100 rows see 356 keys = 6 key tiles, so they are split
+    assert torch.equal(plain[:192].view(torch.int16), split[:192].view(torch.int16))
+    assert not torch.isnan(split.float()).any()
+
+
+def test_prefill_split_padding_rows_untouched():
+    case = W.prefill_case("tailrows_split", 619, lengths=[700, 333], cached=[0, 300])
+    vals = W.materialize(case, DEV)
+    run_store(vals)
+    tq = case.num_new_tokens
+    big_q = torch.zeros((tq + 5, case.num_q_heads, case.head_dim), dtype=torch.bfloat16,
+                        device=DEV)
+    big_q[:tq] = vals["q"]
+    out = torch.full_like(big_q, 7.0)
+    ws = prefill_workspace(case, 128, total_q=tq + 5)
+    pa.pa_prefill_varlen(big_q, vals["k_cache"], vals["v_cache"], vals["cu_seqlens_q"],
+                         vals["cu_seqlens_k"], vals["block_table"], case.max_seqlen_q,
+                         case.max_context_len, case.scale, out, ws, split_keys=128)
+    torch.cuda.synchronize()
+    assert torch.all(out[tq:] == 7.0)
+    assert not torch.isnan(out[:tq].float()).any()

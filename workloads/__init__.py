@@ -173,6 +173,10 @@ def _finish(name, kind, dtype, hq, hkv, d, bs, seed, lengths, cached, shared_pre
     lengths = np.asarray(lengths, dtype=np.int64)
     cached = np.asarray(cached, dtype=np.int64)
     nseq = len(lengths)
+    if len(cached) != nseq or np.any(cached < 0) or np.any(cached > lengths) or \
+            (kind == "prefill" and np.any(cached >= lengths)):
+        raise ValueError(f"{name}: cached positions must lie in [0, length) (prefill) or "
+                         f"[0, length] (decode)")
     shared_blocks = shared_prefix_tokens // bs
     per_seq = []
     for b in range(nseq):
