@@ -425,19 +425,38 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   __shared__ int seq_ctx0[kPrefillPlanMaxSeqs];
   __shared__ int bin_count[kPlanBins];
   __shared__ int bin_base[kPlanBins];
-  __shared__ int scan[kPlanThreads];
+  constexpr int kPlanWaves = kPlanThreads / kWave;
+  __shared__ int wave_sum[kPlanWaves];
   const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
   bin_count[tid] = 0;
   static_assert(kPlanBins == kPlanThreads, "one bin per thread");
+  static_assert(kPlanWaves <= kWave, "wave totals scanned by one wave");
 
-  // Inclusive block scan of scan[] (Hillis-Steele; kPlanThreads entries).
-  auto block_scan = [&]() {
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-      const int add = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
+  // Inclusive scan of x over the block: within each wave by lane shuffles,
+  // then across the wave totals.  Returns this thread's inclusive prefix;
+  // *total receives the block total.
+  auto block_scan = [&](int x, int* total) {
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(x, d, kWave);
+      if (lane >= d) x += y;
     }
+    if (lane == kWave - 1) wave_sum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int v = lane < kPlanWaves ? wave_sum[lane] : 0;
+      for (int d = 1; d < kPlanWaves; d <<= 1) {
+        const int y = __shfl_up(v, d, kWave);
+        if (lane >= d) v += y;
+      }
+      if (lane < kPlanWaves) wave_sum[lane] = v;
+    }
+    __syncthreads();
+    const int excl_waves = wave > 0 ? wave_sum[wave - 1] : 0;
+    *total = wave_sum[kPlanWaves - 1];
+    __syncthreads();  // wave_sum is reused by the next scan
+    return x + excl_waves;
   };
 
   // 1. per sequence: query rows, cached positions, query tiles and the
@@ -458,19 +477,16 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     }
     sum += n_local[k];
   }
-  scan[tid] = sum;
-  __syncthreads();
-  block_scan();
-  int run = scan[tid] - sum;
+  int n_tiles = 0;
+  int run = block_scan(sum, &n_tiles) - sum;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int b = tid * kPer + k;
     if (b < num_seqs) tile_start[b] = run;
     run += n_local[k];
   }
-  if (tid == kPlanThreads - 1) tile_start[num_seqs] = scan[tid];
+  if (tid == 0) tile_start[num_seqs] = n_tiles;
   __syncthreads();
-  const int n_tiles = tile_start[num_seqs];
 
   // Visit every (tile, range): tile i belongs to the last sequence whose first
   // tile is at or before i (sequences without tiles share their successor's
@@ -496,13 +512,9 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   __syncthreads();
   // 3. bin bases for descending weight order, in entries
   const int c = bin_count[kPlanBins - 1 - tid] * num_kv_heads;
-  scan[tid] = c;
-  __syncthreads();
-  block_scan();
-  bin_base[kPlanBins - 1 - tid] = scan[tid] - c;
-  const int n_entries = scan[kPlanThreads - 1];
-  __syncthreads();
-  bin_count[tid] = 0;
+  int n_entries = 0;
+  bin_base[kPlanBins - 1 - tid] = block_scan(c, &n_entries) - c;
+  bin_count[kPlanBins - 1 - tid] = 0;
   __syncthreads();
   // 4. placement: the kv heads of a range take consecutive entries
   for_each_range([&](int b, int qt, int sp, int w) {
