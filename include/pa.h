@@ -175,7 +175,8 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
  * workspace holds, in order and 256-byte aligned: the work-list counter
  * (256 bytes), the work list ((ceil(total_q / R) + num_seqs) * S *
  * num_kv_heads entries of 8 bytes, R = 32 * max(1, 4 / group) query rows per
- * tile), and when S > 1
+ * tile), and when S > 1 the list of split query tiles ((ceil(total_q / R) +
+ * num_seqs) entries of 8 bytes) and
  *
  *   acc [S, total_q, num_q_heads, head_dim]   then
  *   ml  [S, total_q, num_q_heads, 2]

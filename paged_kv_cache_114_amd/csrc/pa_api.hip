@@ -161,18 +161,19 @@ namespace {
 // length; the work list (int2 per item, capacity items); then, when tiles are
 // split, acc [S, total_q, Hq, D] and ml [S, total_q, Hq, 2] floats.
 struct PrefillLayout {
-  size_t items_off, acc_off, ml_off, bytes;
+  size_t items_off, merges_off, acc_off, ml_off, bytes;
 };
 
 PrefillLayout prefill_layout(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim, int32_t splits) {
   auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
   const int64_t rows = pa::prefill_rows_per_tile(num_q_heads / num_kv_heads);
-  const size_t capacity =
-      static_cast<size_t>((total_q + rows - 1) / rows + num_seqs) * splits * num_kv_heads;
+  const size_t tiles = static_cast<size_t>((total_q + rows - 1) / rows + num_seqs);
+  const size_t capacity = tiles * splits * num_kv_heads;
   PrefillLayout l;
   l.items_off = 256;
-  l.acc_off = round256(l.items_off + capacity * 8);
+  l.merges_off = round256(l.items_off + capacity * 8);
+  l.acc_off = round256(l.merges_off + (splits > 1 ? tiles * 8 : 0));
   const size_t slots = splits > 1 ? static_cast<size_t>(splits) * total_q * num_q_heads : 0;
   l.ml_off = round256(l.acc_off + slots * head_dim * sizeof(float));
   l.bytes = round256(l.ml_off + slots * 2 * sizeof(float));
@@ -254,6 +255,7 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
                     head_dim, block_size, max_seqlen_q, max_seqlen_k, total_q, scale,
                     split_keys, splits, static_cast<uint32_t*>(workspace),
                     reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.items_off),
+                    reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.merges_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off),
                     out, out_tok_stride, out_head_stride};

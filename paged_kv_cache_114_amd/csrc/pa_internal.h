@@ -61,6 +61,7 @@ struct PrefillArgs {
   int32_t split_keys, num_splits;  // num_splits == 1: no split, ws_acc / ws_ml unused
   uint32_t* tickets;               // work-list counter and length
   int2* items;                     // work list written by the plan kernel
+  int2* merges;                    // split query tiles, written by the plan kernel
   float* ws_acc;                   // [S, total_q, Hq, D]
   float* ws_ml;                    // [S, total_q, Hq, 2]
   void* out;

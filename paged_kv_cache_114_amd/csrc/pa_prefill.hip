@@ -411,7 +411,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
 // of key tiles the entry covers, largest first (a counting sort; the order
 // among equal weights is arbitrary and does not change any result), the kv
 // heads of one (tile, range) adjacent.  tickets[0] is the claim counter, reset
-// here; tickets[1] the number of entries.
+// here; tickets[1] the number of entries; tickets[2] the number of split
+// query tiles, listed in merges[] for the merge kernel.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 1024;  // weights >= kPlanBins - 1 share the last bin
 
@@ -419,8 +420,9 @@ template <int BM>
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
     int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
-    int2* __restrict__ items) {
+    int2* __restrict__ items, int2* __restrict__ merges) {
   __shared__ int tile_start[kPrefillPlanMaxSeqs + 1];  // first query-tile index per sequence
+  __shared__ int n_merges;
   __shared__ int seq_lq[kPrefillPlanMaxSeqs];
   __shared__ int seq_ctx0[kPrefillPlanMaxSeqs];
   __shared__ int bin_count[kPlanBins];
@@ -431,6 +433,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   bin_count[tid] = 0;
+  if (tid == 0) n_merges = 0;
   static_assert(kPlanBins == kPlanThreads, "one bin per thread");
   static_assert(kPlanWaves <= kWave, "wave totals scanned by one wave");
 
@@ -503,12 +506,12 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
       const int n_kt = (seq_ctx0[b] + min(seq_lq[b], (qt + 1) * BM) - 1) / kBN + 1;
       const int n_split = (n_kt + split_tiles - 1) / split_tiles;
       for (int sp = 0; sp < n_split; ++sp)
-        fn(b, qt, sp, min(min(split_tiles, n_kt - sp * split_tiles), kPlanBins - 1));
+        fn(b, qt, sp, n_split, min(min(split_tiles, n_kt - sp * split_tiles), kPlanBins - 1));
     }
   };
 
   // 2. ranges per weight
-  for_each_range([&](int, int, int, int w) { atomicAdd(&bin_count[w], 1); });
+  for_each_range([&](int, int, int, int, int w) { atomicAdd(&bin_count[w], 1); });
   __syncthreads();
   // 3. bin bases for descending weight order, in entries
   const int c = bin_count[kPlanBins - 1 - tid] * num_kv_heads;
@@ -517,14 +520,17 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   bin_count[kPlanBins - 1 - tid] = 0;
   __syncthreads();
   // 4. placement: the kv heads of a range take consecutive entries
-  for_each_range([&](int b, int qt, int sp, int w) {
+  for_each_range([&](int b, int qt, int sp, int n_split, int w) {
     const int at = bin_base[w] + atomicAdd(&bin_count[w], num_kv_heads);
     for (int g = 0; g < num_kv_heads; ++g)
       items[at + g] = make_int2(b | (g << 16), qt | (sp << 16));
+    if (sp == 0 && n_split > 1) merges[atomicAdd(&n_merges, 1)] = make_int2(b, qt);
   });
+  __syncthreads();
   if (tid == 0) {
     tickets[0] = 0u;
     tickets[1] = static_cast<uint32_t>(n_entries);
+    tickets[2] = static_cast<uint32_t>(n_merges);
   }
 }
 
@@ -546,28 +552,32 @@ struct MergeShape {
 template <int D, int G>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_kv_heads,
-    int32_t split_tiles, const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
-    int32_t total_q, uint16_t* __restrict__ out, int64_t out_tok_stride,
+    const uint32_t* __restrict__ tickets, const int2* __restrict__ merges,
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int32_t total_q,
+    int32_t split_tiles, uint16_t* __restrict__ out, int64_t out_tok_stride,
     int64_t out_head_stride) {
   using S = PrefillShape<D, G>;
   using M = MergeShape<D, G>;
-  const int g = blockIdx.x / M::kParts;
-  const int item = (blockIdx.x % M::kParts) * 256 + threadIdx.x;
-  const int b = blockIdx.y;
+  // Only the split tiles the plan listed are visited: (tile, kv head, part)
+  // pieces are strided over a fixed grid.
+  const int64_t n_work = static_cast<int64_t>(tickets[2]) * num_kv_heads * M::kParts;
+  for (int64_t work = blockIdx.x; work < n_work; work += gridDim.x) {
+  const int part = static_cast<int>(work % M::kParts);
+  const int g = static_cast<int>((work / M::kParts) % num_kv_heads);
+  const int2 tile = merges[work / (static_cast<int64_t>(M::kParts) * num_kv_heads)];
+  const int item = part * 256 + threadIdx.x;
+  const int b = tile.x;
+  const int qt = tile.y;
   const int q_begin = cu_q[b];
   const int lq = cu_q[b + 1] - q_begin;
   const int lk = cu_k[b + 1] - cu_k[b];
-  const int n_qt = (lq + S::kBM - 1) / S::kBM;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.z);
-  if (qt < 0) return;
   const int wg_q0 = qt * S::kBM;
   const int wg_last_pos = lk - lq + min(lq, wg_q0 + S::kBM) - 1;
   const int n_split = (wg_last_pos / kBN + split_tiles) / split_tiles;
-  if (n_split <= 1) return;  // written directly by the prefill kernel
   const int c = item % M::kChunks;
   const int i = (item / M::kChunks) % G;
   const int r = item / (M::kChunks * G);
-  if (wg_q0 + r >= lq) return;
+  if (wg_q0 + r >= lq) continue;
   const int64_t row = q_begin + wg_q0 + r;
   const int64_t head = g * G + i;
   const int64_t num_q_heads = static_cast<int64_t>(num_kv_heads) * G;
@@ -596,19 +606,19 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
                       (static_cast<uint32_t>(f32_to_bf16_rne(o.w * inv)) << 16);
   *reinterpret_cast<uint2*>(out + row * out_tok_stride + head * out_head_stride + 4 * c) =
       make_uint2(lo, hi);
+  }
 }
 
 template <int D, int G>
 hipError_t run(const PrefillArgs& a, hipStream_t stream) {
   using S = PrefillShape<D, G>;
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
-  const int tiles = (a.max_seqlen_q + S::kBM - 1) / S::kBM;
   const size_t bt_bytes = static_cast<size_t>((a.max_seqlen_k + a.block_size - 1) >> bs_log2) * 4;
   // split_tiles >= every tile's key-tile count when nothing is split
   const int split_tiles = a.num_splits > 1 ? a.split_keys / kBN : (a.max_seqlen_k + kBN - 1) / kBN;
   hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
                      a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, split_tiles, a.num_kv_heads,
-                     a.tickets, a.items);
+                     a.tickets, a.items, a.merges);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // one workgroup per resident slot: they stay until the work list is empty
@@ -629,10 +639,9 @@ hipError_t run(const PrefillArgs& a, hipStream_t stream) {
                      a.out_tok_stride, a.out_head_stride);
   err = hipGetLastError();
   if (err != hipSuccess || a.num_splits == 1) return err;
-  hipLaunchKernelGGL((prefill_merge_kernel<D, G>),
-                     dim3(a.num_kv_heads * MergeShape<D, G>::kParts, a.num_seqs, tiles), dim3(256),
-                     0, stream, a.cu_seqlens_q, a.cu_seqlens_k, a.num_kv_heads, split_tiles,
-                     a.ws_acc, a.ws_ml, a.total_q, static_cast<uint16_t*>(a.out),
+  hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(4 * cus), dim3(256), 0, stream,
+                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_kv_heads, a.tickets, a.merges,
+                     a.ws_acc, a.ws_ml, a.total_q, split_tiles, static_cast<uint16_t*>(a.out),
                      a.out_tok_stride, a.out_head_stride);
   return hipGetLastError();
 }

@@ -167,7 +167,8 @@ def test_prefill_workspace_size_formula():
     assert pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 2048)[1] == 1
     nbytes, splits = pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 768)
     items = r256(256 + ((6000 + 63) // 64 + 8) * 3 * 8 * 8)
-    acc = r256(items + 3 * 6000 * 16 * 128 * 4)
+    merges = r256(items + ((6000 + 63) // 64 + 8) * 8)
+    acc = r256(merges + 3 * 6000 * 16 * 128 * 4)
     assert splits == 3 and nbytes == r256(acc + 3 * 6000 * 16 * 2 * 4)
     # group 8: 32-row tiles
     nbytes, _ = pa.pa_prefill_workspace_size(2, 100, 16, 2, 64, 100, 0)
