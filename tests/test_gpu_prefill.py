@@ -194,3 +194,34 @@ def test_prefill_split_padding_rows_untouched():
     torch.cuda.synchronize()
     assert torch.all(out[tq:] == 7.0)
     assert not torch.isnan(out[:tq].float()).any()
+
+
+# ------------------------------------------------------------------ work-list scheduling
+
+def _many_seq_case(name, seed, nseq, lo, hi, bs, hq=16, hkv=8, d=128):
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(lo, hi, size=nseq, endpoint=True)
+    cached = np.where(rng.random(nseq) < 0.2, (lengths * rng.random(nseq)).astype(np.int64), 0)
+    cached = np.minimum(cached, lengths - 1)
+    return W.prefill_case(name, seed, lengths=lengths, cached=cached, hq=hq, hkv=hkv, d=d, bs=bs)
+
+
+@pytest.mark.parametrize("split_keys", [0, 128])
+def test_prefill_many_sequences_more_items_than_workgroups(split_keys):
+    """300 sequences of 1..200 positions, some with cached prefixes: several
+    thousand work entries for 512 resident workgroups, most of them claimed from
+    the counter; sampled sequences against the oracle."""
+    from pa_runner import sample_seqs
+    case = _many_seq_case("many300", 631, 300, 1, 200, 16)
+    seqs = sample_seqs(case, 24, seed=5)
+    _, vals, out = _prefill_vs_oracle(case, seqs=seqs, split_keys=split_keys)
+    assert not torch.isnan(out.float()).any()
+
+
+def test_prefill_largest_supported_batch():
+    """4096 sequences (the plan kernel's limit) of 1..12 positions."""
+    from pa_runner import sample_seqs
+    case = _many_seq_case("many4096", 633, 4096, 1, 12, 8, hq=8, hkv=2, d=64)
+    seqs = sample_seqs(case, 32, seed=7)
+    _, vals, out = _prefill_vs_oracle(case, seqs=seqs)
+    assert not torch.isnan(out.float()).any()
