@@ -229,23 +229,49 @@ __global__ __launch_bounds__(4 * kWave) void decode_reduce_kernel(
   const int h = blockIdx.x * 4 + wave;
   const int b = blockIdx.y;
   if (h >= num_q_heads) return;
-  const int ctx = context_lens[b];
-  const int ns = min(num_splits, (ctx + partition_tokens - 1) / partition_tokens);
   const int64_t base = (static_cast<int64_t>(b) * num_q_heads + h) * num_splits;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + base;
+  const float* acc = ws_acc + base * D + lane * kDpl;
+
+  // The first kPre splits' statistics and partial outputs are loaded together
+  // with the context length instead of after it: the workspace holds
+  // num_splits slots per row, so these loads stay in bounds, and slots past
+  // the row's active splits are loaded but never used.
+  constexpr int kPre = 4;
+  float2 st[kPre];
+  float part[kPre][kDpl];
+#pragma unroll
+  for (int s = 0; s < kPre; ++s)
+    if (s < num_splits) {
+      st[s] = ml[s];
+#pragma unroll
+      for (int k = 0; k < kDpl; ++k) part[s][k] = acc[static_cast<int64_t>(s) * D + k];
+    }
+  const int ctx = context_lens[b];
+  const int ns = min(num_splits, (ctx + partition_tokens - 1) / partition_tokens);
 
   float m_star = -INFINITY;
-  for (int s = lane; s < ns; s += kWave) m_star = fmaxf(m_star, ml[s].x);
+#pragma unroll
+  for (int s = 0; s < kPre; ++s)
+    if (s < ns) m_star = fmaxf(m_star, st[s].x);
+  for (int s = kPre + lane; s < ns; s += kWave) m_star = fmaxf(m_star, ml[s].x);
   m_star = across_groups_max<1>(m_star);
 
   float o[kDpl], lsum = 0.f;
 #pragma unroll
   for (int k = 0; k < kDpl; ++k) o[k] = 0.f;
-  const float* acc = ws_acc + base * D + lane * kDpl;
-  for (int s = 0; s < ns; ++s) {
-    const float2 st = ml[s];
-    const float w = fast_exp2(st.x - m_star);
-    lsum = fmaf(w, st.y, lsum);
+#pragma unroll
+  for (int s = 0; s < kPre; ++s)
+    if (s < ns) {
+      const float w = fast_exp2(st[s].x - m_star);
+      lsum = fmaf(w, st[s].y, lsum);
+#pragma unroll
+      for (int k = 0; k < kDpl; ++k) o[k] = fmaf(w, part[s][k], o[k]);
+    }
+  for (int s = kPre; s < ns; ++s) {
+    const float2 sm = ml[s];
+    const float w = fast_exp2(sm.x - m_star);
+    lsum = fmaf(w, sm.y, lsum);
 #pragma unroll
     for (int k = 0; k < kDpl; ++k) o[k] = fmaf(w, acc[static_cast<int64_t>(s) * D + k], o[k]);
   }
