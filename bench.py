@@ -55,12 +55,13 @@ WORKLOAD_TEXT = {
 def decode_partition(case, cus=256):
     """Split size.  When sequences x kv heads already give every SIMD four waves,
     one split per sequence.  Otherwise 512 tokens (long enough that the reduce is
-    cheap), halved until there is about one (sequence, kv head, split) wave per SIMD."""
+    cheap), halved until there are about two (sequence, kv head, split) waves per
+    SIMD."""
     waves = case.num_seqs * case.num_kv_heads
     if waves >= 16 * cus:
         return 64 * max(1, math.ceil(case.max_context_len / 64))
     p = 512
-    while p > 64 and waves * math.ceil(case.max_context_len / p) < 4 * cus:
+    while p > 64 and waves * math.ceil(case.max_context_len / p) < 8 * cus:
         p //= 2
     return p
 

@@ -19,9 +19,9 @@
 //   kU * 2 KiB of the next tile are in flight while a wave computes, and the
 //   register budget still fits several waves per SIMD.
 // * The workgroup holds NW waves = NW consecutive kv heads of the same
-//   (sequence, split): together they read the contiguous part of each token's
-//   [num_kv_heads, head_dim] row, and they share one staged copy of the
-//   split's block-table entries in LDS.
+//   (sequence, split) -- all 8 at Qwen3's shape: together they read each
+//   token's whole [num_kv_heads, head_dim] row, and they share one staged
+//   copy of the split's block-table entries in LDS.
 // * Online softmax in fp32, base-2 (scores pre-multiplied by log2 e and exp2
 //   on the hardware transcendental unit); the split statistics (m, l, acc)
 //   go to the workspace, and the reduce merges them as [Intro §9.5] requires.
@@ -306,6 +306,7 @@ hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int G>
 hipError_t pick_nw(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_kv_heads % 8 == 0) return run_partition<T, D, G, 8>(a, stream);
   if (a.num_kv_heads % 4 == 0) return run_partition<T, D, G, 4>(a, stream);
   if (a.num_kv_heads % 2 == 0) return run_partition<T, D, G, 2>(a, stream);
   return run_partition<T, D, G, 1>(a, stream);
