@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the prefill work-list claim is one atomic from one lane; without the
+    # wave-level atomic rewrite its result is awaited only where it is used
+    # (the next item), not right after the claim
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

@@ -59,6 +59,8 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBN = 64;  // keys per tile
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle or stride.
+constexpr int kBufferFlags = 0x00020000;
 // v_perm_b32 selector: perm(a, b, sel) picks bytes of {a:b} (b = bytes 0-3);
 // this one keeps the high halves: b.hi | a.hi << 16.
 constexpr uint32_t kPermHigh = 0x07060302u;
@@ -80,6 +82,16 @@ struct PrefillShape {
 
 template <int B>
 struct Buf {};
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = kBegin .. kEnd - 1.
+template <int kBegin, int kEnd, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (kBegin < kEnd) {
+    f(std::integral_constant<int, kBegin>{});
+    static_for<kBegin + 1, kEnd>(f);
+  }
+}
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // LDS position of 16-byte chunk c of a K or V row is c ^ swizzle(row).  The
 // swizzles are chosen per access pattern so that every 32 lanes the LDS serves
@@ -127,21 +139,15 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   __shared__ int ticket_lds;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int half = lane / 32;
   const int col = lane % 32;
 
-  // This lane's DMA rows and source chunks, and its LDS offsets of the MFMA
-  // operands: fixed for the kernel.
-  int dma_row[S::kDmaPerWave], dma_kchunk[S::kDmaPerWave], dma_vchunk[S::kDmaPerWave];
-#pragma unroll
-  for (int i = 0; i < S::kDmaPerWave; ++i) {
-    const int row = (wave * S::kDmaPerWave + i) * S::kRowsPerDma + lane / S::kChunks;
-    dma_row[i] = row;
-    dma_kchunk[i] = (lane % S::kChunks) ^ k_swizzle<D>(row);
-    dma_vchunk[i] = (lane % S::kChunks) ^ v_swizzle<D>(row);
-  }
+  // DMA piece i of this wave fills tile rows piece * kRowsPerDma .. + kRowsPerDma - 1
+  // (piece = wave * kDmaPerWave + i); lane l brings the 16-byte source chunk
+  // that the swizzle puts at LDS position l % kChunks of row l / kChunks.
+  auto dma_row = [&](int i) { return (wave * S::kDmaPerWave + i) * S::kRowsPerDma + lane / S::kChunks; };
   // K operand (A of S^T = K Q^T): row mb*32 + col, chunk 2s + half.
   int k_off[S::kSteps];
 #pragma unroll
@@ -151,18 +157,35 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // lane (half, col) supplies the row of key ks*16 + 8t + 4 half + (col % 16) / 4
   // and dims db*32 + 16 (col / 16) + 4 (col % 4) .. +3; the read hands it the
   // keys ks*16 + 8t + 4 half + e (e = 0..3) of dim db*32 + col.
-  int v_off[2][S::kDB];
+  // The swizzle of key + 8 equals that of key, so read t = 1 sits 8 rows after
+  // read t = 0.
+  int v_off[S::kDB];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int db = 0; db < S::kDB; ++db) {
-      const int key = 8 * t + 4 * half + (col % 16) / 4;
-      const int j4 = col % 4;
-      const int chunk = db * 4 + 2 * (col / 16) + j4 / 2;
-      v_off[t][db] = key * D + 8 * (chunk ^ v_swizzle<D>(key)) + 4 * (j4 % 2);
-    }
+  for (int db = 0; db < S::kDB; ++db) {
+    const int key = 4 * half + (col % 16) / 4;
+    const int j4 = col % 4;
+    const int chunk = db * 4 + 2 * (col / 16) + j4 / 2;
+    v_off[db] = key * D + 8 * (chunk ^ v_swizzle<D>(key)) + 4 * (j4 % 2);
+  }
   const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;  // elements per slot
   const int bs_mask = (1 << bs_log2) - 1;
+  // When a block holds at least a tile (64 tokens), the 64 rows of a tile are
+  // consecutive slots of one block, so a DMA source is one wave-uniform base
+  // plus a per-lane byte offset that is the same for every tile.
+  const bool tile_in_block = bs_log2 >= 6;
+  // Byte offset of a lane's source within the tile: a uniform part for the
+  // piece, (piece * kRowsPerDma) rows, plus a per-lane part.  The V swizzle
+  // depends only on row bits below kRowsPerDma, so its lane part is the same
+  // for every piece.
+  static_assert(S::kRowsPerDma % 4 == 0, "V swizzle must not depend on the piece");
+  const int row_bytes = static_cast<int>(slot_stride) * 2;
+  uint32_t dma_klane[S::kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < S::kDmaPerWave; ++i)
+    dma_klane[i] = (lane / S::kChunks) * row_bytes +
+                   16 * ((lane % S::kChunks) ^ k_swizzle<D>(dma_row(i)));
+  const uint32_t dma_vlane = (lane / S::kChunks) * row_bytes +
+                             16 * ((lane % S::kChunks) ^ v_swizzle<D>(lane / S::kChunks));
 
   // Work entries come from the plan heaviest first, the kv heads of one query
   // tile side by side (they read the same K/V rows, so those DRAM pages are
@@ -175,7 +198,9 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   for (;;) {
   if (tid == 0) ticket_lds = next_entry;
   __syncthreads();
-  const int entry = ticket_lds;
+  // The entry is the same for the whole workgroup: everything derived from it
+  // lives in scalar registers.
+  const int entry = __builtin_amdgcn_readfirstlane(ticket_lds);
   if (entry >= n_entries) break;  // uniform: every wave leaves together
   const int2 item = items[entry];
   const int b = item.x & 0xffff;
@@ -229,22 +254,48 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // lane fetches the source chunk that the swizzle places at its position.
   // Keys past last_pos are masked (past wg_last_pos they are in the future of
   // every row) or belong to the next split; they are fetched from position
-  // last_pos (a readable row), so
-  // P.V only ever multiplies finite values.  K and V of a tile come from the same rows, so each row's slot offset is
-  // computed once for both DMAs.  A lane's row within the tile and its source
-  // chunks are the same for every tile.
-  auto dma_kv = [&](uint16_t* k_lds, uint16_t* v_lds, int kt0) {
+  // last_pos (a readable row), so P.V only ever multiplies finite values.
+  // A lane's row within the tile and its source chunks are the same for every
+  // tile.
+  auto dma = [&](const uint16_t* cache, uint16_t* lds, int kt0, auto is_v) {
+    constexpr bool kV = decltype(is_v)::value;
+    if (tile_in_block && kt0 + kBN - 1 <= last_pos) {
+      const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(kt0 >> bs_log2) - first_blk]);
+      const int64_t tile_off =
+          ((static_cast<int64_t>(blk) << bs_log2) + (kt0 & bs_mask)) * slot_stride +
+          static_cast<int64_t>(g) * D;
+      // a buffer resource over the tile's first row: scalar base, 32-bit lane offsets
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(cache + tile_off), 0, 0x7fffffff, kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < S::kDmaPerWave; ++i) {
-      const int piece = wave * S::kDmaPerWave + i;
-      const int pos = min(kt0 + dma_row[i], last_pos);
-      const int64_t blk = bt_lds[(pos >> bs_log2) - first_blk];
-      const int64_t off = ((blk << bs_log2) + (pos & bs_mask)) * slot_stride +
-                          static_cast<int64_t>(g) * D;
-      const uint16_t* ks = k_cache + off + 8 * dma_kchunk[i];
-      const uint16_t* vs = v_cache + off + 8 * dma_vchunk[i];
-      __builtin_amdgcn_global_load_lds(ks, (lds_void_t*)(k_lds + piece * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs, (lds_void_t*)(v_lds + piece * 512), 16, 0, 0);
+      for (int i = 0; i < S::kDmaPerWave; ++i) {
+        const int piece = wave * S::kDmaPerWave + i;
+        lds_void_t* dst = (lds_void_t*)(lds + piece * 512);
+        const uint32_t voff = kV ? dma_vlane : dma_klane[i];
+        const int soff = piece * S::kRowsPerDma * row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, soff, 0, 0);
+      }
+    } else {
+      // Piece by piece: a piece's kRowsPerDma rows lie in one block (block
+      // sizes are powers of two of at least 8); rows past last_pos are taken
+      // from last_pos, so each piece needs one block-table entry and one
+      // uniform base, and a lane only adds its clamped row.
+#pragma unroll
+      for (int i = 0; i < S::kDmaPerWave; ++i) {
+        const int piece = wave * S::kDmaPerWave + i;
+        const int r0 = min(kt0 + piece * S::kRowsPerDma, last_pos);
+        const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(r0 >> bs_log2) - first_blk]);
+        const int64_t row_off =
+            ((static_cast<int64_t>(blk) << bs_log2) + (r0 & bs_mask)) * slot_stride +
+            static_cast<int64_t>(g) * D;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(cache + row_off), 0, 0x7fffffff, kBufferFlags);
+        const int lane_row = lane / S::kChunks;
+        const int dr = min(lane_row, last_pos - r0);
+        const uint32_t off = (kV ? dma_vlane : dma_klane[i]) + (dr - lane_row) * row_bytes;
+        lds_void_t* dst = (lds_void_t*)(lds + piece * 512);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off, 0, 0, 0);
+      }
     }
   };
 
@@ -258,9 +309,10 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the exponential sum
 
-  auto compute = [&](const uint16_t* kt_lds, const uint16_t* vt_lds, int kt0) {
-    // S^T = K Q^T: the two 32-key accumulator chains are interleaved.
-    f32x16_t acc_s[2] = {f32x16_t{}, f32x16_t{}};
+  // S^T = K Q^T for one 64-key tile: two 32-key accumulator chains.
+  auto qk = [&](const uint16_t* kt_lds, f32x16_t (&acc_s)[2]) {
+    acc_s[0] = f32x16_t{};
+    acc_s[1] = f32x16_t{};
 #pragma unroll
     for (int s = 0; s < S::kSteps; ++s) {
       const uint4 a0 = *reinterpret_cast<const uint4*>(kt_lds + k_off[s]);
@@ -268,9 +320,17 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
       acc_s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[s], acc_s[0], 0, 0, 0);
       acc_s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), qf[s], acc_s[1], 0, 0, 0);
     }
+  };
 
-    // causal mask on tiles that reach past the wave's first position
-    if (kt0 + kBN - 1 > ctx0 + w_q0) {
+  // One tile: S^T = K Q^T, the causal mask where the tile reaches past the
+  // wave's first position, the tile maximum and (rarely) a raised reference
+  // maximum; then P and P.V.  Register e of accumulator mb holds the key
+  // mb * 32 + 8 (e / 4) + (e % 4) + 4 half of the tile for this lane's query.
+  auto compute = [&](const uint16_t* kt_lds, const uint16_t* vt_lds, int kt0) {
+    f32x16_t acc_s[2];
+    qk(kt_lds, acc_s);
+    // a real branch (most tiles need no mask), not 64 selects on every tile
+    if (__builtin_expect(kt0 + kBN - 1 > ctx0 + w_q0, 0)) {
       const int lim = my_pos - kt0 - 4 * half;  // key index (within the tile, sans 4 half) limit
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -278,7 +338,6 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
         for (int r = 0; r < 16; ++r)
           if (mb * 32 + 8 * (r / 4) + (r % 4) > lim) acc_s[mb][r] = -INFINITY;
     }
-
     float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -294,54 +353,86 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
 #pragma unroll
       for (int db = 0; db < S::kDB; ++db) acc_o[db] *= alpha;
     }
-
     // A row of a later split may not have seen a key yet (m_ref = -inf, every
     // score -inf): take its p against 0, which gives 0, instead of NaN.
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+
     // p = 2^(t - m_ref) as a bf16 head (truncated) plus a bf16 remainder,
-    // packed two per word in the order the B operand of P.V wants
-    float psum = 0.f;
+    // packed two per word in the order the B operand of P.V wants: pair pr
+    // holds keys 2 (pr % 8) and 2 (pr % 8) + 1 of accumulator pr / 8, and P.V
+    // step ks (keys 16 ks .. 16 ks + 15) takes pairs 4 ks .. 4 ks + 3.
+    //
+    // The instruction order from here on is fixed by hand: one P.V MFMA per
+    // slot, each slot closed by a scheduling fence, with the slot's share of
+    // the probability work and the V operand reads for MFMAs a few slots
+    // ahead, so the vector ALU forms the probabilities of keys 16 (ks + 1) ..
+    // while the matrix cores multiply those of step ks.  Pairs 0-3 (step 0)
+    // are formed before the first slot.  Within a step the MFMAs go by pairs
+    // of output blocks, head(db), head(db + 1), remainder(db), remainder(db +
+    // 1), so each V operand is live for a few slots only; each accumulator
+    // still takes the head product before the remainder.
+    constexpr int kSlots = 8 * S::kDB;  // P.V MFMAs of the tile
+    constexpr int kDV = 3;              // slots between a V operand read and its first MFMA
+    static_assert(S::kDB % 2 == 0, "output blocks are paired");
+    constexpr auto pv_slot = [](int ks, int db) constexpr {
+      return ks * 2 * S::kDB + 4 * (db / 2) + db % 2;
+    };
+    // half-pair h: exponentials of pair h / 2 for even h, packing for odd h;
+    // -1 = before the first slot
+    constexpr auto half_slot = [](int h) constexpr {
+      return h < 8 ? -1 : (h - 8) * (6 * S::kDB) / 24;
+    };
     uint32_t w_hi[16], w_lo[16];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r + 1], scale_log2, -m_use));
+    float pe[16][2];
+    bf16x8_t va[4][S::kDB];
+    float psum = 0.f;
+    auto half_pair = [&](auto hc) __attribute__((always_inline)) {
+      constexpr int h = decltype(hc)::value;
+      constexpr int pr = h / 2, mb = pr / 8, r = 2 * (pr % 8);
+      if constexpr (h % 2 == 0) {
+        pe[pr][0] = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r], scale_log2, -m_use));
+        pe[pr][1] = __builtin_amdgcn_exp2f(fmaf(acc_s[mb][r + 1], scale_log2, -m_use));
+      } else {
+        const float p0 = pe[pr][0], p1 = pe[pr][1];
         psum += p0 + p1;
         const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
         const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
         const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
-        w_hi[mb * 8 + r / 2] = __builtin_amdgcn_perm(b1, b0, kPermHigh);
-        w_lo[mb * 8 + r / 2] =
-            __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), kPermHigh);
+        w_hi[pr] = __builtin_amdgcn_perm(b1, b0, kPermHigh);
+        w_lo[pr] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), kPermHigh);
       }
+    };
+    auto slot = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int sl = decltype(ic)::value;
+      static_for<0, 4>([&](auto ksc) __attribute__((always_inline)) {
+        static_for<0, S::kDB>([&](auto dbc) __attribute__((always_inline)) {
+          constexpr int ks = decltype(ksc)::value, db = decltype(dbc)::value;
+          if constexpr (cmax(pv_slot(ks, db) - kDV, -1) == sl) {
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(vt_lds + ks * 16 * D + v_off[db]));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(vt_lds + ks * 16 * D + 8 * D + v_off[db]));
+            va[ks][db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        });
+      });
+      if constexpr (sl >= 0) {
+        constexpr int ks = sl / (2 * S::kDB), j = sl % (2 * S::kDB);
+        constexpr int db = 2 * (j / 4) + j % 2;
+        bf16x8_t pb;
+        if constexpr (j % 4 < 2)
+          pb = as_bf16x8(make_uint4(w_hi[4 * ks], w_hi[4 * ks + 1], w_hi[4 * ks + 2], w_hi[4 * ks + 3]));
+        else
+          pb = as_bf16x8(make_uint4(w_lo[4 * ks], w_lo[4 * ks + 1], w_lo[4 * ks + 2], w_lo[4 * ks + 3]));
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][db], pb, acc_o[db], 0, 0, 0);
+      }
+      static_for<0, 32>([&](auto hc) __attribute__((always_inline)) {
+        if constexpr (half_slot(decltype(hc)::value) == sl) half_pair(hc);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<-1, kSlots>(slot);
     l_run += psum;
-
-    // O^T += V^T P^T: kDB independent accumulator chains interleaved; each V
-    // operand (two transpose reads) serves the head and the remainder of P.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t ph = as_bf16x8(
-          make_uint4(w_hi[4 * ks], w_hi[4 * ks + 1], w_hi[4 * ks + 2], w_hi[4 * ks + 3]));
-      const bf16x8_t pl = as_bf16x8(
-          make_uint4(w_lo[4 * ks], w_lo[4 * ks + 1], w_lo[4 * ks + 2], w_lo[4 * ks + 3]));
-      bf16x8_t va[S::kDB];
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db) {
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(vt_lds + ks * 16 * D + v_off[0][db]));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(vt_lds + ks * 16 * D + v_off[1][db]));
-        va[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db)
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], ph, acc_o[db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < S::kDB; ++db)
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pl, acc_o[db], 0, 0, 0);
-    }
   };
 
   // One tile per iteration: start the DMA of the next tile into the other
@@ -358,13 +449,17 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     const int kt0 = kt * kBN;
     if (tid == 0 && kt + 1 == kt_end)
       next_entry = static_cast<int>(gridDim.x + atomicAdd(tickets, 1u));
-    if (kt + 1 < kt_end) dma_kv(k_nxt, v_nxt, kt0 + kBN);
+    if (kt + 1 < kt_end) {
+      dma(k_cache, k_nxt, kt0 + kBN, std::false_type{});
+      dma(v_cache, v_nxt, kt0 + kBN, std::true_type{});
+    }
     if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0);  // else: all in this wave's future
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  dma_kv(k_lds0, v_lds0, kt_begin * kBN);
+  dma(k_cache, k_lds0, kt_begin * kBN, std::false_type{});
+  dma(v_cache, v_lds0, kt_begin * kBN, std::true_type{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
