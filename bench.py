@@ -325,6 +325,69 @@ def cpu_baseline(name, budget_s=12.0):
             "cpu": cpu, "seconds": round(elapsed, 2)}
 
 
+def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch=None):
+    """A decode step of a layers-deep model at one workload's shapes: per layer,
+    store + partition + reduce on that layer's own cache, all on one stream.
+    Timed eager (3 launches per layer) and as one captured HIP graph replay."""
+    import torch
+
+    import paged_kv_cache_114_amd as pa
+    import workloads as W
+    case = W.FULL_CASES[name]() if batch is None else W.c2_decode(
+        batch=batch, name=f"c2_decode_b{batch}")
+    base = W.materialize(case, "cuda:0")
+    p = partition or decode_partition(case)
+    nbytes, splits = pa.pa_decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim,
+                                                 case.max_context_len, p)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    lays = []
+    for _ in range(layers):
+        lays.append(dict(base, k_cache=base["k_cache"].clone(), v_cache=base["v_cache"].clone(),
+                         out=torch.empty_like(base["q"])))
+
+    def step():
+        for lay in lays:
+            pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
+                           lay["slot_mapping"])
+            pa.pa_decode(lay["q"], lay["k_cache"], lay["v_cache"], lay["block_table"],
+                         lay["context_lens"], case.max_context_len, p, case.scale, ws)
+            pa.pa_decode_reduce(ws, lay["context_lens"], splits, p, lay["out"])
+
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda:0")
+
+    def timed(fn):
+        ev = HipEvents(2 * (steps + warmup))
+        for i in range(warmup + steps):
+            sink.copy_(flush_buf.sum())
+            ev.record(2 * i)
+            fn()
+            ev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        return sum(ev.ms(2 * i, 2 * i + 1) for i in range(warmup, warmup + steps)) / steps
+
+    eager_ms = timed(step)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph_ms = timed(graph.replay)
+    kv = layers * case.kv_bytes_logical()
+    return {"workload": f"{case.name} x {layers} layers (store + decode + reduce per layer)",
+            "layers": layers, "launches_per_step": 3 * layers,
+            "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
+            "graph_speedup": round(eager_ms / graph_ms, 3),
+            "kv_GBps_graph": round(kv / (graph_ms * 1e-3) / 1e9, 1),
+            "kv_GBps_eager": round(kv / (eager_ms * 1e-3) / 1e9, 1),
+            "partition_tokens": p}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +466,12 @@ def main():
                 torch.cuda.empty_cache()
             except Exception as e:  # a workload whose kernel is missing is reported as such
                 also[name] = {"error": f"{type(e).__name__}: {e}"}
+        for key, batch in (("c2_graph28", None), ("c2_b4_graph28", 4)):
+            try:
+                also[key] = graph_decode("c2", 28, steps=max(5, args.steps // 2), batch=batch)
+                torch.cuda.empty_cache()
+            except Exception as e:
+                also[key] = {"error": f"{type(e).__name__}: {e}"}
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,

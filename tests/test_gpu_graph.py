@@ -1,0 +1,162 @@
+"""A decode step of a 28-layer model (per layer: store the new K/V rows, the
+split-K partition pass, the reduce) captured as one HIP graph.  The library only
+enqueues kernels on the caller's stream -- no allocation, no memset, no host
+synchronisation -- so the whole step records into a graph.  Batches are padded
+to a bucket size with rows that store nothing (slot -1) and read nothing
+(context 0).  Every replay must equal the eager launches bit for bit, also after
+the inputs change in place; sampled layers are checked against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from pa_runner import DEV, HostInputs, assert_close, decode_buffers, to_f64
+
+import paged_kv_cache_114_amd as pa
+
+pytestmark = pytest.mark.gpu
+
+LAYERS = 28
+
+
+def make_layers(case, n, seed):
+    """n layers with the same block table and lengths; each layer has its own
+    caches (copies of the drawn pool), queries and new rows."""
+    base = W.materialize(case, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    tdt = W._torch_dtype(case.dtype)
+    layers = []
+    for _ in range(n):
+        lay = dict(base)
+        lay["k_cache"] = base["k_cache"].clone()
+        lay["v_cache"] = base["v_cache"].clone()
+        for key in ("q", "k_new", "v_new"):
+            lay[key] = torch.randn(base[key].shape, generator=gen, device=DEV).to(tdt)
+        lay["out"] = torch.empty_like(base["q"])
+        layers.append(lay)
+    return layers
+
+
+def decode_step(case, layers, ws, splits, partition):
+    for lay in layers:
+        pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
+                       lay["slot_mapping"])
+        pa.pa_decode(lay["q"], lay["k_cache"], lay["v_cache"], lay["block_table"],
+                     lay["context_lens"], case.max_context_len, partition, case.scale, ws)
+        pa.pa_decode_reduce(ws, lay["context_lens"], splits, partition, lay["out"])
+
+
+@pytest.mark.parametrize("lengths,pad", [
+    ([1000, 17, 300, 513, 256, 1, 64, 700, 129, 900, 2], 5),   # 11 sequences in bucket 16
+    ([40], 0),                                                  # bucket 1
+])
+def test_graph_decode_step_replays_equal_eager(lengths, pad):
+    case = W.decode_case(f"graph_{len(lengths)}", 91, lengths=lengths, pad_rows=pad)
+    print(f"graph case={case.name} B={case.num_seqs} layers={LAYERS}", flush=True)
+    partition = 256
+    layers = make_layers(case, LAYERS, seed=7)
+    ws, _, splits = decode_buffers(case, partition)
+
+    decode_step(case, layers, ws, splits, partition)
+    torch.cuda.synchronize()
+    eager = [lay["out"].clone() for lay in layers]
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_step(case, layers, ws, splits, partition)   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        decode_step(case, layers, ws, splits, partition)
+    torch.cuda.synchronize()
+
+    bits = torch.int16
+    for rep in range(3):
+        for lay in layers:                                   # eager work between replays
+            lay["out"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, lay in enumerate(layers):
+            assert torch.equal(lay["out"].view(bits), eager[i].view(bits)), (rep, i)
+
+    # new queries in place: the replay sees them
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(8)
+    for lay in layers:
+        lay["q"].copy_(torch.randn(lay["q"].shape, generator=gen, device=DEV))
+    decode_step(case, layers, ws, splits, partition)
+    torch.cuda.synchronize()
+    eager2 = [lay["out"].clone() for lay in layers]
+    for lay in layers:
+        lay["out"].fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    for i, lay in enumerate(layers):
+        assert torch.equal(lay["out"].view(bits), eager2[i].view(bits)), i
+
+    # padding rows give zeros; sampled layers against the oracle
+    real = len(lengths)
+    pool = W.materialize(case, DEV)   # the pool as it was before this step's store
+    for i in (0, LAYERS - 1):
+        lay = layers[i]
+        got = to_f64(lay["out"], case.dtype)
+        if pad:
+            assert np.array_equal(got[real:], np.zeros_like(got[real:]))
+        pre = dict(lay, k_cache=pool["k_cache"], v_cache=pool["v_cache"])
+        host = HostInputs(case, pre, list(range(real)))
+        assert_close(got[:real], host.decode(), case.dtype, f"layer {i}")
+
+
+def test_graph_prefill_step_replays_equal_eager():
+    """Four layers of a varlen prefill (store, then the work-list plan, the
+    persistent tile kernel and, with key-range splits, the merge): the plan kernel
+    resets its own counter on the device, so every replay redoes the whole
+    schedule; replays equal the eager launches bit for bit."""
+    case = W.prefill_case("graph_prefill", 92, lengths=[700, 300, 1100, 64], cached=[0, 256, 300, 0])
+    print(f"graph prefill case={case.name}", flush=True)
+    layers = make_layers(case, 4, seed=9)
+    for split_keys in (0, 256):
+        nbytes, _ = pa.pa_prefill_workspace_size(case.num_seqs, case.num_new_tokens,
+                                                 case.num_q_heads, case.num_kv_heads,
+                                                 case.head_dim, case.max_context_len, split_keys)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+
+        def step():
+            for lay in layers:
+                pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
+                               lay["slot_mapping"])
+                pa.pa_prefill_varlen(lay["q"], lay["k_cache"], lay["v_cache"],
+                                     lay["cu_seqlens_q"], lay["cu_seqlens_k"],
+                                     lay["block_table"], case.max_seqlen_q, case.max_context_len,
+                                     case.scale, lay["out"], ws, split_keys=split_keys)
+
+        step()
+        torch.cuda.synchronize()
+        eager = [lay["out"].clone() for lay in layers]
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for lay in layers:
+                lay["out"].fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for i, lay in enumerate(layers):
+                assert torch.equal(lay["out"].view(torch.int16), eager[i].view(torch.int16)), \
+                    (split_keys, rep, i)
+    pool = W.materialize(case, DEV)
+    host = HostInputs(case, dict(layers[0], k_cache=pool["k_cache"], v_cache=pool["v_cache"]))
+    assert_close(to_f64(layers[0]["out"], case.dtype), host.prefill(), case.dtype, "layer 0")
