@@ -49,6 +49,9 @@ WORKLOAD_TEXT = {
           "block 256, random block placement",
     "c5": "skewed shared-prefix decode: batch 256, block 16, 192 sequences share a 2048-token "
           "prefix + lognormal tails (median 300, cap 6000), 64 private U[32,8192]",
+    "mixed": "one chunked-prefill engine step through the varlen prefill call: 48 decode rows "
+             "(contexts U[128,1024], Lq=1), 4 chunks of 512 after unaligned cached prefixes "
+             "U[100,1500], 2 fresh prompts U[64,700]; 16q/8kv, d=128, bf16, block 256",
 }
 
 
@@ -456,7 +459,7 @@ def main():
 
     also = {}
     if not args.no_also:
-        for name in ("c4", "c5", "c3"):
+        for name in ("c4", "c5", "c3", "mixed"):
             if name == args.workload:
                 continue
             try:

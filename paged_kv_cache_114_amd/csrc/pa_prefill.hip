@@ -24,10 +24,12 @@
 //   read), whose per-16-lane transpose hands every lane 4 keys of one dim;
 //   the keys are chosen to match the order in which the score accumulator
 //   holds P, so no data is permuted anywhere.
-// * Each p is split into a bf16 head and a bf16 remainder (p - head) and both
-//   go through the P.V MFMA, so P carries ~16 significant bits instead of
-//   bf16's 8: with bf16 P alone, rows whose weighted values cancel can miss
-//   a 2e-3 absolute error bound.  This costs half again the MFMA work.
+// * P enters the P.V MFMA as bf16.  Rows that see at least 256 keys round p
+//   to nearest; a wave whose rows see fewer also sends p's remainder (p minus
+//   its truncated bf16 head) through the MFMA, so P carries ~16 significant
+//   bits: with few keys the weight sits on a few values, and bf16 P alone can
+//   miss the 2e-3 absolute bound where they cancel.  The remainder costs half
+//   again the P.V work, so only those waves pay it.
 // * K/V tiles go from HBM straight into LDS by DMA (global_load_lds, 16 bytes
 //   a lane), double-buffered: the next tile streams in while the MFMAs read the
 //   current one, with no registers or VALU spent on staging and one barrier
@@ -55,10 +57,15 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBN = 64;  // keys per tile
+// Rows whose first position sees fewer keys than this carry the remainder of
+// p through P.V (see short_rows).
+constexpr int kRestKeys = 256;
 // Word 3 of a raw buffer resource: 32-bit data format, no swizzle or stride.
 constexpr int kBufferFlags = 0x00020000;
 // v_perm_b32 selector: perm(a, b, sel) picks bytes of {a:b} (b = bytes 0-3);
@@ -228,6 +235,12 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   const bool row_ok = my_row < lq;
   const int my_pos = ctx0 + my_row;                         // its position in the sequence
   const int w_last_pos = ctx0 + min(lq - 1, w_q0 + 31);     // last position the wave needs
+  // A row that sees fewer than kRestKeys keys can put most of its weight on a
+  // few of them, where rounding p to bf16 (relative error up to 2^-9) can move
+  // the output by more than the 2e-3 absolute bound when the weighted values
+  // cancel; such waves carry p's remainder through P.V as well.  Rows that see
+  // more keys take p rounded to nearest bf16, as FlashAttention does.
+  const bool short_rows = ctx0 + w_q0 + 1 < kRestKeys;
 
   // Only keys kt_begin * 64 .. last_pos are ever loaded, so the entries of
   // their blocks are all the workgroup needs.
@@ -326,7 +339,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // wave's first position, the tile maximum and (rarely) a raised reference
   // maximum; then P and P.V.  Register e of accumulator mb holds the key
   // mb * 32 + 8 (e / 4) + (e % 4) + 4 half of the tile for this lane's query.
-  auto compute = [&](const uint16_t* kt_lds, const uint16_t* vt_lds, int kt0) {
+  auto compute = [&](const uint16_t* kt_lds, const uint16_t* vt_lds, int kt0, auto with_rest) {
+    constexpr bool kRest = decltype(with_rest)::value;
     f32x16_t acc_s[2];
     qk(kt_lds, acc_s);
     // a real branch (most tiles need no mask), not 64 selects on every tile
@@ -357,10 +371,11 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     // score -inf): take its p against 0, which gives 0, instead of NaN.
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 
-    // p = 2^(t - m_ref) as a bf16 head (truncated) plus a bf16 remainder,
-    // packed two per word in the order the B operand of P.V wants: pair pr
-    // holds keys 2 (pr % 8) and 2 (pr % 8) + 1 of accumulator pr / 8, and P.V
-    // step ks (keys 16 ks .. 16 ks + 15) takes pairs 4 ks .. 4 ks + 3.
+    // With kRest, p = 2^(t - m_ref) goes in as a bf16 head (truncated) plus a
+    // bf16 remainder (~16 significant bits); without, as p rounded to nearest
+    // bf16.  Packed two per word in the order the B operand of P.V wants: pair
+    // pr holds keys 2 (pr % 8) and 2 (pr % 8) + 1 of accumulator pr / 8, and
+    // P.V step ks (keys 16 ks .. 16 ks + 15) takes pairs 4 ks .. 4 ks + 3.
     //
     // The instruction order from here on is fixed by hand: one P.V MFMA per
     // slot, each slot closed by a scheduling fence, with the slot's share of
@@ -371,16 +386,17 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     // of output blocks, head(db), head(db + 1), remainder(db), remainder(db +
     // 1), so each V operand is live for a few slots only; each accumulator
     // still takes the head product before the remainder.
-    constexpr int kSlots = 8 * S::kDB;  // P.V MFMAs of the tile
-    constexpr int kDV = 3;              // slots between a V operand read and its first MFMA
+    constexpr int kPer = kRest ? 2 : 1;       // MFMAs per output block and 16 keys
+    constexpr int kSlots = 4 * kPer * S::kDB;  // P.V MFMAs of the tile
+    constexpr int kDV = 3;                     // slots between a V operand read and its first MFMA
     static_assert(S::kDB % 2 == 0, "output blocks are paired");
     constexpr auto pv_slot = [](int ks, int db) constexpr {
-      return ks * 2 * S::kDB + 4 * (db / 2) + db % 2;
+      return kRest ? ks * 2 * S::kDB + 4 * (db / 2) + db % 2 : ks * S::kDB + db;
     };
     // half-pair h: exponentials of pair h / 2 for even h, packing for odd h;
     // -1 = before the first slot
     constexpr auto half_slot = [](int h) constexpr {
-      return h < 8 ? -1 : (h - 8) * (6 * S::kDB) / 24;
+      return h < 8 ? -1 : (h - 8) * (3 * kPer * S::kDB) / 24;
     };
     uint32_t w_hi[16], w_lo[16];
     float pe[16][2];
@@ -395,11 +411,15 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
       } else {
         const float p0 = pe[pr][0], p1 = pe[pr][1];
         psum += p0 + p1;
-        const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-        const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
-        const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
-        w_hi[pr] = __builtin_amdgcn_perm(b1, b0, kPermHigh);
-        w_lo[pr] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), kPermHigh);
+        if constexpr (kRest) {
+          const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+          const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+          const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+          w_hi[pr] = __builtin_amdgcn_perm(b1, b0, kPermHigh);
+          w_lo[pr] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), kPermHigh);
+        } else {
+          w_hi[pr] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t));
+        }
       }
     };
     auto slot = [&](auto ic) __attribute__((always_inline)) {
@@ -417,10 +437,10 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
         });
       });
       if constexpr (sl >= 0) {
-        constexpr int ks = sl / (2 * S::kDB), j = sl % (2 * S::kDB);
-        constexpr int db = 2 * (j / 4) + j % 2;
+        constexpr int ks = sl / (kPer * S::kDB), j = sl % (kPer * S::kDB);
+        constexpr int db = kRest ? 2 * (j / 4) + j % 2 : j;
         bf16x8_t pb;
-        if constexpr (j % 4 < 2)
+        if constexpr (!kRest || j % 4 < 2)
           pb = as_bf16x8(make_uint4(w_hi[4 * ks], w_hi[4 * ks + 1], w_hi[4 * ks + 2], w_hi[4 * ks + 3]));
         else
           pb = as_bf16x8(make_uint4(w_lo[4 * ks], w_lo[4 * ks + 1], w_lo[4 * ks + 2], w_lo[4 * ks + 3]));
@@ -440,7 +460,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // since), multiply the current one, then wait for this wave's DMA and meet
   // at the barrier.  Buffers are chosen at compile time (the loop is unrolled
   // by two) so the compiler can tell the DMA target from the buffer being read.
-  auto iteration = [&](int kt, auto buf) {
+  auto iteration = [&](int kt, auto buf, auto with_rest) {
     constexpr bool kFirst = std::is_same<decltype(buf), Buf<0>>::value;
     const uint16_t* k_cur = kFirst ? k_lds0 : k_lds1;
     const uint16_t* v_cur = kFirst ? v_lds0 : v_lds1;
@@ -453,7 +473,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
       dma(k_cache, k_nxt, kt0 + kBN, std::false_type{});
       dma(v_cache, v_nxt, kt0 + kBN, std::true_type{});
     }
-    if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0);  // else: all in this wave's future
+    if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0, with_rest);  // else: all in this wave's future
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -462,10 +482,18 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   dma(v_cache, v_lds0, kt_begin * kBN, std::true_type{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = kt_begin; kt < kt_end; kt += 2) {
-    iteration(kt, Buf<0>{});
-    if (kt + 1 < kt_end) iteration(kt + 1, Buf<1>{});
-  }
+  // One loop per kind of wave (the waves of a workgroup may run different
+  // copies; both meet the same barriers once per tile).
+  auto key_loop = [&](auto with_rest) {
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+      iteration(kt, Buf<0>{}, with_rest);
+      if (kt + 1 < kt_end) iteration(kt + 1, Buf<1>{}, with_rest);
+    }
+  };
+  if (short_rows)
+    key_loop(std::true_type{});
+  else
+    key_loop(std::false_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (row_ok && n_split > 1) {

@@ -284,12 +284,30 @@ def c5_shared_prefix_decode(batch=256, n_shared=192, prefix=2048, tail_median=30
                        shared_seqs=shared.tolist())
 
 
+def mixed_batch(n_decode=48, n_chunks=4, chunk=512, n_fresh=2, seed=1146,
+                name="mixed_chunked_b54") -> Case:
+    """One engine step with chunked prefill, through the varlen prefill call: n_decode
+    sequences decoding one token (contexts U[128, 1024], Lq = 1), n_chunks long
+    prompts continuing by one chunk of `chunk` positions after a cached prefix
+    U[100, 1500] that is generally not block aligned, and n_fresh new prompts
+    U[64, 700].  Qwen3-0.6B head shapes, block 256."""
+    rng = np.random.default_rng(seed)
+    dec = rng.integers(128, 1024, size=n_decode, endpoint=True)
+    cached_chunks = rng.integers(100, 1500, size=n_chunks, endpoint=True)
+    fresh = rng.integers(64, 700, size=n_fresh, endpoint=True)
+    lengths = np.concatenate([dec, cached_chunks + chunk, fresh])
+    cached = np.concatenate([dec - 1, cached_chunks, np.zeros(n_fresh, np.int64)])
+    return prefill_case(name, seed, lengths=lengths, cached=cached,
+                        notes={"rows": "decode rows (Lq=1), chunked-prefill continuations, fresh prompts"})
+
+
 FULL_CASES = {
     "c1": c1_tiny_decode,
     "c2": c2_decode,
     "c3": c3_prefill,
     "c4": c4_heavy_decode,
     "c5": c5_shared_prefix_decode,
+    "mixed": mixed_batch,
 }
 
 # Scaled-down twins: same head shapes, block sizes and length laws, several
@@ -303,6 +321,8 @@ SMALL_CASES = {
     "c5s": lambda: c5_shared_prefix_decode(batch=12, n_shared=9, prefix=512, tail_cap=1500,
                                            private_hi=2048, seed=2145,
                                            name="c5s_shared_prefix_b12"),
+    "mixeds": lambda: mixed_batch(n_decode=10, n_chunks=3, chunk=200, n_fresh=2, seed=2146,
+                                  name="mixeds_chunked_b15"),
 }
 
 
