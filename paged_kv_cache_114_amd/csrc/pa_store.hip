@@ -5,9 +5,12 @@
 // cache; a slot of -1 is a padding row and is skipped.  The source may be a
 // strided view (token and head strides), the point of [Pico #6, pitfall 1].
 //
-// Work is flattened over (token, K|V, head, word) so consecutive lanes move
-// consecutive 16-byte words of one head row: every wave reads and writes whole
-// contiguous segments, which is all an HBM-bound copy needs.
+// One wave moves one (token, K or V) row: num_kv_heads * head_dim elements,
+// read as W-sized words.  The slot is loaded once per row and is uniform over
+// the wave (a padding row is skipped whole).  Lane l takes words l, l + 64,
+// ...; each lane issues all of its loads before its first store, so a wave
+// keeps the whole row in flight.  A word's head is word >> hw_log2
+// (head_dim * element size / sizeof(W) is a power of two).
 
 #include "pa_common.h"
 #include "pa_internal.h"
@@ -15,44 +18,65 @@
 namespace pa {
 namespace {
 
+constexpr int kStoreWaves = 4;  // waves per workgroup
+constexpr int kStoreUnroll = 2; // words per lane whose loads are issued together
+                                // (a Qwen3 row of 8 heads x 128 bf16 is 2 per lane)
+
 template <typename W>
-__global__ __launch_bounds__(256) void store_kernel(
+__global__ __launch_bounds__(kStoreWaves* kWave) void store_kernel(
     const char* __restrict__ k, const char* __restrict__ v, int64_t k_tok_b, int64_t k_head_b,
     int64_t v_tok_b, int64_t v_head_b, char* __restrict__ k_cache, char* __restrict__ v_cache,
-    const int32_t* __restrict__ slot_mapping, uint32_t total, uint32_t per_tensor,
-    uint32_t words_per_head, int64_t row_bytes, int64_t head_bytes) {
-  // total = tokens * 2 * per_tensor < 2^31 (checked on the host)
-  for (uint32_t item = blockIdx.x * blockDim.x + threadIdx.x; item < total;
-       item += gridDim.x * blockDim.x) {
-    const uint32_t tok = item / (2 * per_tensor);
-    const uint32_t rem = item - tok * 2 * per_tensor;
-    const bool is_v = rem >= per_tensor;
-    const uint32_t c = is_v ? rem - per_tensor : rem;
-    const uint32_t head = c / words_per_head;
-    const uint32_t word = c - head * words_per_head;
+    const int32_t* __restrict__ slot_mapping, int32_t rows, int32_t words_per_row,
+    int32_t hw_log2, int64_t row_bytes, int64_t head_bytes) {
+  const int lane = threadIdx.x % kWave;
+  const int hw_mask = (1 << hw_log2) - 1;
+  for (int r = blockIdx.x * kStoreWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+       r < rows; r += gridDim.x * kStoreWaves) {
+    const int tok = r >> 1;
+    const bool is_v = r & 1;
     const int32_t slot = slot_mapping[tok];
     if (slot < 0) continue;  // -1: padding row, nothing to write
-    const char* src = is_v ? v + tok * v_tok_b + head * v_head_b : k + tok * k_tok_b + head * k_head_b;
-    char* dst = (is_v ? v_cache : k_cache) + static_cast<int64_t>(slot) * row_bytes + head * head_bytes;
-    reinterpret_cast<W*>(dst)[word] = reinterpret_cast<const W*>(src)[word];
+    const char* src = is_v ? v + tok * v_tok_b : k + tok * k_tok_b;
+    const int64_t head_b = is_v ? v_head_b : k_head_b;
+    char* dst = (is_v ? v_cache : k_cache) + static_cast<int64_t>(slot) * row_bytes;
+    for (int w0 = 0; w0 < words_per_row; w0 += kStoreUnroll * kWave) {
+      // No lane branches: a lane past the row re-reads its last word and writes
+      // the same value back, so the loads issue back to back and the wave waits
+      // once before its stores.
+      W val[kStoreUnroll];
+#pragma unroll
+      for (int u = 0; u < kStoreUnroll; ++u) {
+        const int w = min(w0 + u * kWave + lane, words_per_row - 1);
+        val[u] = *reinterpret_cast<const W*>(src + (w >> hw_log2) * head_b +
+                                             (w & hw_mask) * static_cast<int64_t>(sizeof(W)));
+      }
+#pragma unroll
+      for (int u = 0; u < kStoreUnroll; ++u) {
+        const int w = min(w0 + u * kWave + lane, words_per_row - 1);
+        *reinterpret_cast<W*>(dst + (w >> hw_log2) * head_bytes +
+                              (w & hw_mask) * static_cast<int64_t>(sizeof(W))) = val[u];
+      }
+    }
   }
 }
 
 template <typename W>
 hipError_t run(const StoreArgs& a, hipStream_t stream) {
   const int64_t eb = a.elt_bytes;
-  const uint32_t words_per_head = static_cast<uint32_t>(a.head_dim * eb / sizeof(W));
-  const uint32_t per_tensor = static_cast<uint32_t>(a.num_kv_heads) * words_per_head;
-  const int64_t total = static_cast<int64_t>(a.num_tokens) * 2 * per_tensor;
-  if (total >= (int64_t{1} << 31)) return hipErrorInvalidValue;
-  const int64_t want = (total + 255) / 256;
+  const int words_per_head = static_cast<int>(a.head_dim * eb / sizeof(W));
+  const int hw_log2 = __builtin_ctz(static_cast<unsigned>(words_per_head));
+  if ((1 << hw_log2) != words_per_head) return hipErrorInvalidValue;
+  const int words_per_row = a.num_kv_heads * words_per_head;
+  const int64_t rows = int64_t{a.num_tokens} * 2;
+  if (rows >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+  const int64_t want = (rows + kStoreWaves - 1) / kStoreWaves;
   const int blocks = static_cast<int>(want < 16384 ? (want > 0 ? want : 1) : 16384);
-  hipLaunchKernelGGL(store_kernel<W>, dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(store_kernel<W>, dim3(blocks), dim3(kStoreWaves * kWave), 0, stream,
                      static_cast<const char*>(a.k), static_cast<const char*>(a.v),
                      a.k_tok_stride * eb, a.k_head_stride * eb, a.v_tok_stride * eb,
                      a.v_head_stride * eb, static_cast<char*>(a.k_cache),
-                     static_cast<char*>(a.v_cache), a.slot_mapping, static_cast<uint32_t>(total),
-                     per_tensor, words_per_head, static_cast<int64_t>(a.num_kv_heads) * a.head_dim * eb,
+                     static_cast<char*>(a.v_cache), a.slot_mapping, static_cast<int32_t>(rows),
+                     words_per_row, hw_log2, static_cast<int64_t>(a.num_kv_heads) * a.head_dim * eb,
                      static_cast<int64_t>(a.head_dim) * eb);
   return hipGetLastError();
 }
