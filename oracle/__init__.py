@@ -17,3 +17,12 @@ from .paged_attention import (  # noqa: F401
     store,
     to_f64,
 )
+from .norm_rope import (  # noqa: F401
+    qk_norm_rope,
+    qk_norm_rope_store,
+    rms_norm,
+    rope,
+    rope_frequencies,
+    rotate_pair,
+    split_qkv,
+)
