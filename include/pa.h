@@ -2,7 +2,8 @@
  * pa.h -- C ABI of the MI355X (gfx950) paged KV-cache attention library.
  *
  * The library implements the attention step of a nano-vLLM-style inference
- * engine over a paged KV cache: storing this step's K/V rows through a slot
+ * engine over a paged KV cache: the per-head q/k norm and rotary embedding
+ * that precede the cache, storing this step's K/V rows through a slot
  * mapping, variable-length causal prefill, and batched single-token decode
  * with a split-K (flash-decoding) partition plus a reduce.
  *
@@ -10,13 +11,16 @@
  *   [Intro]   "大模型推理入门与 nano-vLLM 源码详解" (duanmeng.github.io)
  *   [Pico #6] "Pico-vLLM 开发日志 #6" on Fain's blog (koas-w.github.io)
  *   [Log-walk] "对着日志读懂 nano-vllm" (juejin.cn)
+ *   [Pico #8] "Pico-vLLM 开发日志 #8 更多Triton Kernel和性能优化" (koas-w.github.io)
+ *   [Analysis] "nano-vllm 技术分析" (deepseek.csdn.net)
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Pointers named *_cache, q, k, v, out, workspace, slot_mapping,
- *   block_table, context_lens, cu_seqlens_* are DEVICE pointers; every other
- *   argument is a host value.  The caller owns all memory (the library never
- *   allocates, frees, synchronises, or reads device memory from the host).
+ * - Pointers named *_cache, q, k, v, qkv, q_out, *_weight, out, workspace,
+ *   slot_mapping, positions, block_table, context_lens, cu_seqlens_* are
+ *   DEVICE pointers; every other argument is a host value.  The caller owns
+ *   all memory (the library never allocates, frees, synchronises, or reads
+ *   device memory from the host).
  *   All work is enqueued on `stream` (may be 0 for the null stream); launch
  *   shapes depend only on host arguments, so calls can be captured in a HIP
  *   graph.
@@ -24,8 +28,8 @@
  *   k_cache, v_cache are contiguous [num_blocks, block_size, num_kv_heads,
  *   head_dim] arrays of `dtype`.  Slot s is block s / block_size, offset
  *   s % block_size [Intro §9.2].
- * - dtype: PA_DTYPE_F32 or PA_DTYPE_BF16.  q, k, v, caches and out all share
- *   it.  Arithmetic is fp32 throughout; outputs are rounded to `dtype`
+ * - dtype: PA_DTYPE_F32 or PA_DTYPE_BF16.  q, k, v, qkv, q_out, the norm
+ *   weights, caches and out all share it.  Arithmetic is fp32 throughout; outputs are rounded to `dtype`
  *   (round to nearest even for bf16).
  * - head_dim in {64, 128}; block_size a power of two in [8, 1024];
  *   num_q_heads a multiple of num_kv_heads with a group size
@@ -96,6 +100,49 @@ int pa_store_kv(const void* k, const void* v, int64_t k_tok_stride, int64_t k_he
                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                 int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
                 hipStream_t stream);
+
+/*
+ * pa_qk_norm_rope_store -- per-head q/k RMSNorm, rotary position embedding,
+ * and the store of this step's rotated K and raw V into the paged cache.
+ *
+ * Defined by [Intro §12.2, §19.3, §19.7], [Analysis §4.2, §4.4] ("nano-vllm
+ * 技术分析", deepseek.csdn.net) and the fused RoPE + cache-store kernel of
+ * [Pico #8 §1] ("Pico-vLLM 开发日志 #8"): token t's projection row holds
+ * num_q_heads Q heads, then num_kv_heads K heads, then num_kv_heads V heads,
+ * head_dim features each.  Every Q and K head x becomes
+ *   y_i = gamma_i * x_i / sqrt(mean_j(x_j^2) + eps)      (gamma: q_norm_weight
+ * for Q heads, k_norm_weight for K heads; both NULL: y = x, the model without
+ * q/k norm), then each pair (y_i, y_{i+d/2}), i < d/2, is turned by
+ * phi = positions[t] * rope_theta^(-2i/d) radians:
+ *   y_i' = y_i cos(phi) - y_{i+d/2} sin(phi),  y_{i+d/2}' = y_i sin(phi) + y_{i+d/2} cos(phi).
+ * Rotated Q goes to q_out[t]; rotated K and the V row, copied bit for bit, go
+ * to slot s = slot_mapping[t] as pa_store_kv writes them (s = -1: K and V are
+ * not written, q_out[t] still is).  Arithmetic is fp32 (the angle and its
+ * reduction to one turn are fp64); each result is rounded once to dtype.
+ *
+ *   qkv             [num_tokens, >= (num_q_heads + 2 * num_kv_heads) * head_dim]
+ *                   of dtype, row stride qkv_tok_stride (elements).
+ *   q_norm_weight,  [head_dim] of dtype each, or both NULL.
+ *   k_norm_weight
+ *   positions       int32 [num_tokens], the tokens' logical positions (any value).
+ *   slot_mapping    int32 [num_tokens] as for pa_store_kv.
+ *   q_out           [num_tokens, num_q_heads, head_dim] of dtype, row stride
+ *                   q_out_tok_stride >= num_q_heads * head_dim; it may be the Q
+ *                   part of qkv itself (same rows: an in-place update), no other
+ *                   overlap.
+ *   k_cache, v_cache  as in the conventions.
+ * eps must be finite and >= 0, rope_theta finite and > 0.  head_dim 64 or 128;
+ * any num_q_heads, num_kv_heads >= 1 (no head reads another here, so the
+ * group-size rule does not apply).  Every device pointer and both strides (in
+ * bytes) must be 16-byte aligned.  num_tokens == 0 is a no-op.
+ */
+int pa_qk_norm_rope_store(const void* qkv, int64_t qkv_tok_stride, const void* q_norm_weight,
+                          const void* k_norm_weight, const int32_t* positions,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float eps, double rope_theta,
+                          void* q_out, int64_t q_out_tok_stride, void* k_cache, void* v_cache,
+                          int32_t block_size, int64_t num_blocks, int32_t dtype,
+                          hipStream_t stream);
 
 /*
  * pa_decode_workspace_size -- host-only helper for pa_decode.

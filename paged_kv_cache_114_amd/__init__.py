@@ -29,6 +29,7 @@ EXPORTS = (
     "pa_version",
     "pa_strerror",
     "pa_store_kv",
+    "pa_qk_norm_rope_store",
     "pa_decode_workspace_size",
     "pa_decode",
     "pa_decode_reduce",
@@ -56,6 +57,9 @@ def _load():
     lib.pa_store_kv.restype = ctypes.c_int
     lib.pa_store_kv.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, i32, i32, i32, i32, i64,
                                 i32, vp]
+    lib.pa_qk_norm_rope_store.restype = ctypes.c_int
+    lib.pa_qk_norm_rope_store.argtypes = [vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                          ctypes.c_double, vp, i64, vp, vp, i32, i64, i32, vp]
     lib.pa_decode_workspace_size.restype = ctypes.c_int
     lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz),
                                              ctypes.POINTER(i32)]
@@ -125,6 +129,23 @@ def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
         _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1), _ptr(k_cache),
         _ptr(v_cache), _ptr(slot_mapping), slot_mapping.shape[0], hkv, d, bs, nb,
         _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, positions, slot_mapping,
+                          num_q_heads, num_kv_heads, eps, rope_theta, q_out, k_cache, v_cache,
+                          stream=None) -> None:
+    """Per-head q/k RMSNorm + RoPE of ``qkv [T, (Hq + 2 Hkv) d]``; writes ``q_out [T, Hq, d]``
+    and stores rotated K and raw V at ``slot_mapping`` in ``[NB, bs, Hkv, d]`` caches.
+    Both norm weights ``None``: rotation only."""
+    nb, bs, hkv, d = k_cache.shape
+    assert hkv == num_kv_heads, "cache head count differs from num_kv_heads"
+    assert qkv.stride(-1) == 1 and q_out.stride(-1) == 1, "innermost stride must be 1"
+    assert q_out.dim() == 3 and q_out.stride(1) == d, "q_out must be [T, Hq, d] with head stride d"
+    _check("pa_qk_norm_rope_store", library().pa_qk_norm_rope_store(
+        _ptr(qkv), qkv.stride(0), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions),
+        _ptr(slot_mapping), qkv.shape[0], num_q_heads, num_kv_heads, d, eps, rope_theta,
+        _ptr(q_out), q_out.stride(0), _ptr(k_cache), _ptr(v_cache), bs, nb, _dtype_code(qkv),
+        _stream(stream)))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,

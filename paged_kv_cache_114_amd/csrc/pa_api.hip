@@ -68,6 +68,41 @@ int pa_store_kv(const void* k, const void* v, int64_t k_tok_stride, int64_t k_he
   return launched(pa::launch_store(a, stream));
 }
 
+int pa_qk_norm_rope_store(const void* qkv, int64_t qkv_tok_stride, const void* q_norm_weight,
+                          const void* k_norm_weight, const int32_t* positions,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float eps, double rope_theta,
+                          void* q_out, int64_t q_out_tok_stride, void* k_cache, void* v_cache,
+                          int32_t block_size, int64_t num_blocks, int32_t dtype,
+                          hipStream_t stream) {
+  const int eb = elt_bytes(dtype);
+  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  const int64_t heads = int64_t{num_q_heads} + 2 * int64_t{num_kv_heads};
+  if (heads > 65536) return PA_ERR_UNSUPPORTED;
+  if (qkv_tok_stride < heads * head_dim || q_out_tok_stride < int64_t{num_q_heads} * head_dim)
+    return PA_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !(eps <= 3.4e38f)) return PA_ERR_INVALID_ARG;   // NaN or infinite
+  if (!(rope_theta > 0.0) || !(rope_theta <= 1.7e308)) return PA_ERR_INVALID_ARG;
+  if ((q_norm_weight == nullptr) != (k_norm_weight == nullptr)) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!qkv || !positions || !slot_mapping || !q_out || !k_cache || !v_cache)
+    return PA_ERR_INVALID_ARG;
+  if (num_blocks > (INT32_MAX / block_size) + int64_t{1}) return PA_ERR_UNSUPPORTED;  // int32 slots
+  if (!aligned16(qkv) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (qkv_tok_stride * eb) % 16 || (q_out_tok_stride * eb) % 16)
+    return PA_ERR_UNSUPPORTED;
+  if (q_norm_weight && (!aligned16(q_norm_weight) || !aligned16(k_norm_weight)))
+    return PA_ERR_UNSUPPORTED;
+  pa::RopeArgs a{qkv, qkv_tok_stride, q_norm_weight, k_norm_weight, positions, slot_mapping,
+                 num_tokens, num_q_heads, num_kv_heads, head_dim, eps, rope_theta, q_out,
+                 q_out_tok_stride, k_cache, v_cache, eb};
+  return launched(pa::launch_norm_rope_store(a, stream));
+}
+
 int pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                              int32_t max_context_len, int32_t partition_tokens, size_t* bytes,
                              int32_t* num_splits) {

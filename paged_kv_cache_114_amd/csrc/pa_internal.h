@@ -69,6 +69,24 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+struct RopeArgs {
+  const void* qkv;
+  int64_t qkv_tok_stride;
+  const void* q_weight;  // both null: no q/k norm
+  const void* k_weight;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  int32_t num_tokens, num_q_heads, num_kv_heads, head_dim;
+  float eps;
+  double theta;
+  void* q_out;
+  int64_t q_out_tok_stride;
+  void* k_cache;
+  void* v_cache;
+  int32_t elt_bytes;
+};
+hipError_t launch_norm_rope_store(const RopeArgs& a, hipStream_t stream);
+
 // The prefill work list is built by one workgroup that holds a per-sequence
 // table in LDS, which bounds the batch.
 constexpr int kPrefillPlanMaxSeqs = 4096;

@@ -190,3 +190,42 @@ def test_prefill_split_validation():
     assert prefill(b=5000, ws=fake, wsb=big, **ptrs) == pa.PA_ERR_UNSUPPORTED    # > 4096 seqs
     assert prefill(sk=64, bs=8, mk=8 * 65536, mq=8 * 8192, tq=8 * 8192, ws=fake, wsb=big,
                    **ptrs) == pa.PA_ERR_UNSUPPORTED                  # > 32767 key ranges
+
+
+def rope(**kw):
+    args = dict(qkv=NULL, qs=4096, qw=NULL, kw=NULL, pos=NULL, slots=NULL, t=4, hq=16, hkv=8,
+                d=128, eps=1e-6, theta=1e6, q=NULL, qos=2048, kc=NULL, vc=NULL, bs=256, nb=10,
+                dtype=BF16)
+    args.update(kw)
+    a = args
+    return pa.library().pa_qk_norm_rope_store(
+        a["qkv"], a["qs"], a["qw"], a["kw"], a["pos"], a["slots"], a["t"], a["hq"], a["hkv"],
+        a["d"], a["eps"], a["theta"], a["q"], a["qos"], a["kc"], a["vc"], a["bs"], a["nb"],
+        a["dtype"], NULL)
+
+
+def test_norm_rope_store_validation():
+    fake = ctypes.c_void_p(256)
+    ptrs = dict(qkv=fake, pos=fake, slots=fake, q=fake, kc=fake, vc=fake)
+    assert rope() == pa.PA_ERR_INVALID_ARG                         # null pointers
+    assert rope(t=0) == pa.PA_OK                                   # nothing to do
+    assert rope(t=-1) == pa.PA_ERR_INVALID_ARG
+    assert rope(d=96) == pa.PA_ERR_UNSUPPORTED
+    assert rope(bs=100) == pa.PA_ERR_UNSUPPORTED
+    assert rope(dtype=5) == pa.PA_ERR_UNSUPPORTED
+    assert rope(hkv=0) == pa.PA_ERR_INVALID_ARG
+    assert rope(qs=4000) == pa.PA_ERR_INVALID_ARG                  # row shorter than Q, K, V
+    assert rope(qos=1024) == pa.PA_ERR_INVALID_ARG                 # q_out row too short
+    assert rope(eps=-1.0) == pa.PA_ERR_INVALID_ARG
+    assert rope(eps=float("nan")) == pa.PA_ERR_INVALID_ARG
+    assert rope(eps=float("inf")) == pa.PA_ERR_INVALID_ARG
+    assert rope(theta=0.0) == pa.PA_ERR_INVALID_ARG
+    assert rope(theta=float("inf")) == pa.PA_ERR_INVALID_ARG
+    assert rope(qw=fake, **ptrs) == pa.PA_ERR_INVALID_ARG          # one weight without the other
+    assert rope(kw=fake, **ptrs) == pa.PA_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(258)
+    assert rope(**dict(ptrs, qkv=odd)) == pa.PA_ERR_UNSUPPORTED    # misaligned projection rows
+    assert rope(qs=4100, **ptrs) == pa.PA_ERR_UNSUPPORTED          # row stride not 16-byte
+    assert rope(qw=odd, kw=fake, **ptrs) == pa.PA_ERR_UNSUPPORTED  # misaligned weights
+    # group sizes the attention kernels reject are fine here
+    assert rope(hq=12, hkv=2, qs=16 * 128, qos=12 * 128, t=0) == pa.PA_OK

@@ -1,0 +1,163 @@
+"""pa_qk_norm_rope_store on the GPU against the oracle (q/k head RMSNorm, RoPE,
+and the paged store of rotated K and raw V).
+
+Q and the stored K are compared element by element within the floating-point
+bound; V and every slot the step must not write are compared bit for bit over
+the whole pool (the NaN poison in unused slots included).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from pa_runner import DEV
+
+import paged_kv_cache_114_amd as pa
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6          # Qwen3's rms_norm_eps
+THETA = 1e6         # Qwen3's rope_theta
+
+
+def pair_bound(ref, dtype):
+    """Per-element bound.  bf16: 2e-3 + 1e-2 |ref| (the output's own rounding is
+    at most 2^-9 |ref|).  fp32: 1e-5 (1 + |pair|), with |pair| the length of the
+    rotation pair the element belongs to -- the fp32 angle and norm errors scale
+    with it, not with the element, which can cancel to zero."""
+    if dtype == "bf16":
+        return 2e-3 + 1e-2 * np.abs(ref)
+    half = ref.shape[-1] // 2
+    length = np.hypot(ref[..., :half], ref[..., half:])
+    return 1e-5 * (1.0 + np.concatenate([length, length], axis=-1))
+
+
+def check(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bad = err > pair_bound(ref, dtype)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} out of bound, max err "
+                           f"{err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}")
+    return float(err.max())
+
+
+def run_case(case, *, use_norm=True, row_pad=0, in_place=False, positions=None, slots=None):
+    """Run the HIP step and the oracle on the same inputs; compare everything."""
+    dt = case.dtype
+    hq, hkv, d = case.num_q_heads, case.num_kv_heads, case.head_dim
+    t = case.num_new_tokens
+    print(f"rope case={case.name} T={t} Hq={hq} Hkv={hkv} d={d} {dt} norm={use_norm} "
+          f"pad={row_pad} in_place={in_place}", flush=True)
+    vals = W.materialize(case, DEV)
+    inp = W.projection_inputs(case, DEV, row_pad=row_pad)
+    if positions is not None:
+        inp["positions"] = torch.tensor(positions, dtype=torch.int32, device=DEV)
+    if slots is not None:
+        inp["slot_mapping"] = torch.tensor(slots, dtype=torch.int32, device=DEV)
+    qkv = inp["qkv"]
+    qw = inp["q_norm_weight"] if use_norm else None
+    kw = inp["k_norm_weight"] if use_norm else None
+    # oracle inputs: host copies of the inputs, taken before the kernel runs
+    qkv_raw = W.raw_numpy(qkv, dt)
+    qw_raw = W.raw_numpy(qw, dt) if use_norm else None
+    kw_raw = W.raw_numpy(kw, dt) if use_norm else None
+    k_before = W.raw_numpy(vals["k_cache"], dt)
+    v_before = W.raw_numpy(vals["v_cache"], dt)
+    pos_h = inp["positions"].cpu().numpy()
+    slot_h = inp["slot_mapping"].cpu().numpy()
+
+    if in_place:
+        q_out = qkv[:, :hq * d].view(t, hq, d)
+    else:
+        q_out = torch.full((t, hq, d), float("nan"), dtype=qkv.dtype, device=DEV)
+    pa.pa_qk_norm_rope_store(qkv, qw, kw, inp["positions"], inp["slot_mapping"], hq, hkv, EPS,
+                             THETA, q_out, vals["k_cache"], vals["v_cache"])
+    torch.cuda.synchronize()
+
+    q_rot, k_rot, k_want, v_want = oracle.qk_norm_rope_store(
+        qkv_raw, dt, hq, hkv, d, qw_raw, kw_raw, pos_h, slot_h, EPS, THETA, k_before, v_before)
+    err_q = check(oracle.to_f64(W.raw_numpy(q_out, dt), dt), q_rot, dt, "q_out")
+    k_after = W.raw_numpy(vals["k_cache"], dt)
+    written = slot_h[slot_h >= 0]
+    bs = case.block_size
+    err_k = 0.0
+    if len(written):
+        got_k = oracle.to_f64(k_after[written // bs, written % bs], dt)
+        err_k = check(got_k, k_want[written // bs, written % bs], dt, "stored K")
+    keep = np.ones(k_after.shape[0] * bs, dtype=bool)
+    keep[written] = False
+    flat = lambda a: a.reshape(a.shape[0] * bs, -1)  # noqa: E731
+    assert np.array_equal(flat(k_after)[keep], flat(k_before)[keep]), "K slots outside the step"
+    assert np.array_equal(W.raw_numpy(vals["v_cache"], dt), v_want), "V cache (bitwise)"
+    if in_place:  # the K/V part of the row is left as it was
+        assert np.array_equal(W.raw_numpy(qkv, dt)[:, hq * d:], qkv_raw[:, hq * d:])
+    print(f"  max err q {err_q:.2e} k {err_k:.2e}", flush=True)
+    return err_q, err_k
+
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "mixeds"])
+def test_norm_rope_store_small(name):
+    run_case(W.SMALL_CASES[name]())
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "mixed"])
+def test_norm_rope_store_full(name):
+    """Full-size workloads (the whole token set; the oracle is vectorised)."""
+    run_case(W.FULL_CASES[name]())
+
+
+def test_without_norm_weights_rotation_only():
+    """Both weights absent: the model without q/k norm (rotation only)."""
+    run_case(W.SMALL_CASES["c3s"](), use_norm=False)
+    run_case(W.SMALL_CASES["c1"](), use_norm=False)
+
+
+def test_in_place_q_and_padded_rows():
+    """q_out aliasing the Q part of a row-padded projection buffer."""
+    case = W.SMALL_CASES["mixeds"]()
+    run_case(case, in_place=True, row_pad=64)
+    run_case(W.SMALL_CASES["c1"](), in_place=True, row_pad=4)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [
+    (12, 2, 128, "bf16"),   # Qwen2.5-1.5B heads: a pass mixes Q, K and V heads
+    (32, 8, 128, "bf16"),   # 48 head slots: two load chunks
+    (3, 1, 64, "f32"),      # fewer head slots than one pass holds
+    (40, 8, 64, "bf16"),    # d = 64 with a ragged last pass
+])
+def test_head_layouts(hq, hkv, d, dtype):
+    case = W.prefill_case(f"heads_{hq}_{hkv}_{d}", 3100 + hq, lengths=[70, 300, 33],
+                          cached=[0, 256, 0], hq=hq, hkv=hkv, d=d, dtype=dtype, bs=16)
+    run_case(case)
+
+
+def test_positions_far_and_negative_and_padding_slots():
+    """Large and negative positions (the angle's range reduction) and -1 slots
+    (K and V skipped, Q still written)."""
+    case = W.decode_case("far", 3200, lengths=[5, 40960, 300, 2, 77, 1000])
+    t = case.num_new_tokens
+    positions = [0, 40959, 2**31 - 1, -5, 1 << 20, 123456789][:t]
+    slots = case.slot_mapping.copy()
+    slots[[1, 4]] = -1
+    run_case(case, positions=positions, slots=slots)
+    case32 = W.decode_case("far32", 3201, lengths=[5, 40960, 300], dtype="f32", d=64, hq=4,
+                           hkv=2, bs=16)
+    run_case(case32, positions=[7, 2**31 - 1, -40000])
+
+
+def test_zero_tokens_is_a_no_op():
+    case = W.SMALL_CASES["c2s"]()
+    vals = W.materialize(case, DEV)
+    k_before = W.raw_numpy(vals["k_cache"], case.dtype)
+    empty = torch.empty((0, 32 * 128), dtype=torch.bfloat16, device=DEV)
+    e32 = torch.empty((0,), dtype=torch.int32, device=DEV)
+    q_out = torch.empty((0, 16, 128), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(128, dtype=torch.bfloat16, device=DEV)
+    pa.pa_qk_norm_rope_store(empty, w, w, e32, e32, 16, 8, EPS, THETA, q_out, vals["k_cache"],
+                             vals["v_cache"])
+    torch.cuda.synchronize()
+    assert np.array_equal(W.raw_numpy(vals["k_cache"], case.dtype), k_before)

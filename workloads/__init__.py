@@ -405,3 +405,36 @@ def from_raw(raw: np.ndarray, dtype, device="cpu"):
     signed = raw.view(np.int16 if dtype == "bf16" else np.int32)
     t = torch.from_numpy(np.ascontiguousarray(signed)).to(device)
     return t.view(_torch_dtype(dtype))
+
+
+def projection_inputs(case: Case, device="cpu", row_pad=0) -> dict:
+    """Draw the fused projection rows and q/k norm weights of ``case``'s new tokens.
+
+    The input of the norm + rotary + store step: ``qkv`` ``[T, (Hq + 2 Hkv) d
+    + row_pad]`` (Q heads, then K, then V, as a fused projection writes them;
+    ``row_pad`` extra columns widen the row stride) with entries ``N(0, 1)``
+    rounded to the storage type, and ``q_norm_weight, k_norm_weight`` ``[d]``
+    uniform in [0.25, 2] (positive per-feature gains around one, as learned
+    norm weights are), all from a ``torch.Generator`` seeded with
+    ``case.seed + 7919`` on ``device`` in that order; ``positions`` are the new
+    tokens' logical positions and ``slot_mapping`` their write slots (int32).
+    """
+    import torch
+    dev = torch.device(device)
+    tdt = _torch_dtype(case.dtype)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(case.seed + 7919)
+    hq, hkv, d = case.num_q_heads, case.num_kv_heads, case.head_dim
+    t = case.num_new_tokens
+    width = (hq + 2 * hkv) * d
+    qkv = torch.randn((t, width + row_pad), generator=gen, device=dev,
+                      dtype=torch.float32).to(tdt)
+    qw = (0.25 + 1.75 * torch.rand((d,), generator=gen, device=dev, dtype=torch.float32)).to(tdt)
+    kw = (0.25 + 1.75 * torch.rand((d,), generator=gen, device=dev, dtype=torch.float32)).to(tdt)
+    i32 = dict(dtype=torch.int32, device=dev)
+    return {
+        "qkv": qkv[:, :width] if row_pad else qkv,
+        "q_norm_weight": qw, "k_norm_weight": kw,
+        "positions": torch.tensor(case.new_pos, **i32),
+        "slot_mapping": torch.tensor(case.slot_mapping, **i32),
+    }
