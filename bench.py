@@ -434,10 +434,13 @@ def cpu_baseline(name, budget_s=12.0, all_cores_s=8.0):
             "cpu": cpu, "seconds": round(elapsed, 2), "all_cores": all_cores}
 
 
-def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch=None):
+def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch=None,
+                 fused=False):
     """A decode step of a layers-deep model at one workload's shapes: per layer,
     store + partition + reduce on that layer's own cache, all on one stream.
-    Timed eager (3 launches per layer) and as one captured HIP graph replay."""
+    Timed eager (3 launches per layer) and as one captured HIP graph replay.
+    ``fused``: the store is the q/k norm + rope + store step on the layer's
+    projection rows, and the decode reads the rotated Q it writes."""
     import torch
 
     import paged_kv_cache_114_amd as pa
@@ -449,16 +452,25 @@ def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch
     nbytes, splits = pa.pa_decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim,
                                                  case.max_context_len, p)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    proj = W.projection_inputs(case, "cuda:0") if fused else {}
+    hq, hkv = case.num_q_heads, case.num_kv_heads
     lays = []
     for _ in range(layers):
         lays.append(dict(base, k_cache=base["k_cache"].clone(), v_cache=base["v_cache"].clone(),
-                         out=torch.empty_like(base["q"])))
+                         out=torch.empty_like(base["q"]), q_rot=torch.empty_like(base["q"])))
 
     def step():
         for lay in lays:
-            pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
-                           lay["slot_mapping"])
-            pa.pa_decode(lay["q"], lay["k_cache"], lay["v_cache"], lay["block_table"],
+            if fused:
+                pa.pa_qk_norm_rope_store(proj["qkv"], proj["q_norm_weight"],
+                                         proj["k_norm_weight"], proj["positions"],
+                                         proj["slot_mapping"], hq, hkv, 1e-6, 1e6, lay["q_rot"],
+                                         lay["k_cache"], lay["v_cache"])
+            else:
+                pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
+                               lay["slot_mapping"])
+            pa.pa_decode(lay["q_rot"] if fused else lay["q"], lay["k_cache"], lay["v_cache"],
+                         lay["block_table"],
                          lay["context_lens"], case.max_context_len, p, case.scale, ws)
             pa.pa_decode_reduce(ws, lay["context_lens"], splits, p, lay["out"])
 
@@ -488,13 +500,48 @@ def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch
     torch.cuda.synchronize()
     graph_ms = timed(graph.replay)
     kv = layers * case.kv_bytes_logical()
-    return {"workload": f"{case.name} x {layers} layers (store + decode + reduce per layer)",
+    first = "q/k norm + rope + store" if fused else "store"
+    return {"workload": f"{case.name} x {layers} layers ({first} + decode + reduce per layer)",
             "layers": layers, "launches_per_step": 3 * layers,
             "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
             "graph_speedup": round(eager_ms / graph_ms, 3),
             "kv_GBps_graph": round(kv / (graph_ms * 1e-3) / 1e9, 1),
             "kv_GBps_eager": round(kv / (eager_ms * 1e-3) / 1e9, 1),
             "partition_tokens": p}
+
+
+def norm_rope_store(name, steps=15, warmup=3):
+    """The per-head q/k RMSNorm + RoPE + paged store step over one workload's new
+    tokens (its fused projection rows), timed alone with HIP events after a
+    cache flush.  Algorithmic bytes per token: the projection row read once
+    ((Hq + 2 Hkv) d elements) and written once (Q to q_out, K and V to the
+    cache), plus its position and slot (8 bytes)."""
+    import torch
+
+    import paged_kv_cache_114_amd as pa
+    import workloads as W
+    case = W.FULL_CASES[name]()
+    vals = W.materialize(case, "cuda:0")
+    inp = W.projection_inputs(case, "cuda:0")
+    t, hq, hkv, d = case.num_new_tokens, case.num_q_heads, case.num_kv_heads, case.head_dim
+    q_out = torch.empty((t, hq, d), dtype=inp["qkv"].dtype, device="cuda:0")
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda:0")
+    ev = HipEvents(2 * (steps + warmup))
+    for i in range(warmup + steps):
+        sink.copy_(flush_buf.sum())
+        ev.record(2 * i)
+        pa.pa_qk_norm_rope_store(inp["qkv"], inp["q_norm_weight"], inp["k_norm_weight"],
+                                 inp["positions"], inp["slot_mapping"], hq, hkv, 1e-6, 1e6,
+                                 q_out, vals["k_cache"], vals["v_cache"])
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    ms = sum(ev.ms(2 * i, 2 * i + 1) for i in range(warmup, warmup + steps)) / steps
+    nbytes = t * (2 * (hq + 2 * hkv) * d * case.elt_bytes + 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{case.name} new tokens (q/k norm + rope + store)", "tokens": t,
+            "kernel_ms": round(ms, 5), "algorithmic_bytes": nbytes, "GBps": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -575,9 +622,17 @@ def main():
                 torch.cuda.empty_cache()
             except Exception as e:  # a workload whose kernel is missing is reported as such
                 also[name] = {"error": f"{type(e).__name__}: {e}"}
-        for key, batch in (("c2_graph28", None), ("c2_b4_graph28", 4)):
+        for name in ("c2", "c3", "mixed"):
             try:
-                also[key] = graph_decode("c2", 28, steps=max(5, args.steps // 2), batch=batch)
+                also[f"norm_rope_store_{name}"] = norm_rope_store(name, max(5, args.steps // 2))
+                torch.cuda.empty_cache()
+            except Exception as e:
+                also[f"norm_rope_store_{name}"] = {"error": f"{type(e).__name__}: {e}"}
+        for key, batch, fused in (("c2_graph28", None, False), ("c2_b4_graph28", 4, False),
+                                  ("c2_graph28_fused_rope", None, True)):
+            try:
+                also[key] = graph_decode("c2", 28, steps=max(5, args.steps // 2), batch=batch,
+                                         fused=fused)
                 torch.cuda.empty_cache()
             except Exception as e:
                 also[key] = {"error": f"{type(e).__name__}: {e}"}

@@ -160,3 +160,66 @@ def test_graph_prefill_step_replays_equal_eager():
     pool = W.materialize(case, DEV)
     host = HostInputs(case, dict(layers[0], k_cache=pool["k_cache"], v_cache=pool["v_cache"]))
     assert_close(to_f64(layers[0]["out"], case.dtype), host.prefill(), case.dtype, "layer 0")
+
+
+def test_graph_fused_rope_decode_step_replays_equal_eager():
+    """The decode step as an engine runs it per layer: q/k norm + rope + store
+    from the layer's projection rows, then the partition pass and the reduce
+    over the rotated Q.  Captured for 28 layers; replays equal the eager
+    launches bit for bit (rotated Q, outputs and caches), and a sampled layer's
+    rotated Q matches the oracle."""
+    import oracle
+    case = W.decode_case("graph_fused", 93, lengths=[1000, 17, 300, 513, 1, 64], pad_rows=2)
+    print(f"graph fused case={case.name} B={case.num_seqs} layers={LAYERS}", flush=True)
+    hq, hkv, d, dt = case.num_q_heads, case.num_kv_heads, case.head_dim, case.dtype
+    partition = 256
+    layers = make_layers(case, LAYERS, seed=10)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    proj = W.projection_inputs(case, DEV)
+    for lay in layers:
+        lay["qkv"] = torch.randn(proj["qkv"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+        lay["q_rot"] = torch.empty_like(lay["q"])
+    ws, _, splits = decode_buffers(case, partition)
+
+    def step():
+        for lay in layers:
+            pa.pa_qk_norm_rope_store(lay["qkv"], proj["q_norm_weight"], proj["k_norm_weight"],
+                                     proj["positions"], proj["slot_mapping"], hq, hkv, 1e-6, 1e6,
+                                     lay["q_rot"], lay["k_cache"], lay["v_cache"])
+            pa.pa_decode(lay["q_rot"], lay["k_cache"], lay["v_cache"], lay["block_table"],
+                         lay["context_lens"], case.max_context_len, partition, case.scale, ws)
+            pa.pa_decode_reduce(ws, lay["context_lens"], splits, partition, lay["out"])
+
+    qkv0 = W.raw_numpy(layers[0]["qkv"], dt)
+    step()
+    torch.cuda.synchronize()
+    keys = ("q_rot", "out", "k_cache", "v_cache")
+    eager = [{k: lay[k].clone() for k in keys} for lay in layers]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for lay in layers:
+            lay["out"].fill_(float("nan"))
+            lay["q_rot"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, lay in enumerate(layers):
+            for k in keys:
+                assert torch.equal(lay[k].view(torch.int16), eager[i][k].view(torch.int16)), \
+                    (rep, i, k)
+    q_rot, _, _, _ = oracle.qk_norm_rope_store(
+        qkv0, dt, hq, hkv, d, W.raw_numpy(proj["q_norm_weight"], dt),
+        W.raw_numpy(proj["k_norm_weight"], dt), proj["positions"].cpu().numpy(),
+        np.full(case.num_new_tokens, -1), 1e-6, 1e6,
+        np.zeros((1, 1, hkv, d), np.uint16), np.zeros((1, 1, hkv, d), np.uint16))
+    assert_close(to_f64(layers[0]["q_rot"], dt), q_rot, dt, "layer 0 rotated q")

@@ -123,15 +123,23 @@ def test_in_place_q_and_padded_rows():
     run_case(W.SMALL_CASES["c1"](), in_place=True, row_pad=4)
 
 
-@pytest.mark.parametrize("hq,hkv,d,dtype", [
-    (12, 2, 128, "bf16"),   # Qwen2.5-1.5B heads: a pass mixes Q, K and V heads
-    (32, 8, 128, "bf16"),   # 48 head slots: two load chunks
-    (3, 1, 64, "f32"),      # fewer head slots than one pass holds
-    (40, 8, 64, "bf16"),    # d = 64 with a ragged last pass
+SHORT = ([70, 300, 33], [0, 256, 0])       # 147 tokens
+LONG = ([700, 1200, 333], [0, 100, 0])      # 2133 tokens: several waves per compute unit
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype,rows", [
+    (12, 2, 128, "bf16", SHORT),   # Qwen2.5-1.5B heads: a pass mixes Q, K and V heads
+    (32, 8, 128, "bf16", SHORT),   # 48 head slots, six passes
+    (32, 8, 128, "bf16", LONG),
+    (3, 1, 64, "f32", SHORT),      # fewer head slots than one pass holds
+    (40, 8, 64, "bf16", SHORT),    # d = 64 with a ragged last pass
+    (40, 8, 64, "bf16", LONG),
+    (16, 8, 128, "f32", LONG),     # fp32 rows (two 16-byte words per half)
 ])
-def test_head_layouts(hq, hkv, d, dtype):
-    case = W.prefill_case(f"heads_{hq}_{hkv}_{d}", 3100 + hq, lengths=[70, 300, 33],
-                          cached=[0, 256, 0], hq=hq, hkv=hkv, d=d, dtype=dtype, bs=16)
+def test_head_layouts(hq, hkv, d, dtype, rows):
+    lengths, cached = rows
+    case = W.prefill_case(f"heads_{hq}_{hkv}_{d}_{sum(lengths)}", 3100 + hq, lengths=lengths,
+                          cached=cached, hq=hq, hkv=hkv, d=d, dtype=dtype, bs=16)
     run_case(case)
 
 
