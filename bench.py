@@ -15,10 +15,13 @@ in [128, 1024], block 256, bf16).  `value` is its KV read rate: the K and V
 bytes the step must read (sum of context lengths x 8 kv heads x 128 x 2 x 2
 bytes) over the measured step time.  The JSON line also carries the roofline
 of the dominant kernel (decode partition pass), the oracle's CPU rate on a
-bounded sample, and (under "also") the heavy decode, the shared-prefix decode
-and the varlen prefill workloads measured the same way.
+bounded sample, and (under "also") the heavy decode, the shared-prefix decode,
+the varlen prefill and the mixed chunked-prefill workloads measured the same
+way, the q/k norm + rope + store step over three workloads' new tokens, and
+28-layer decode steps replayed as HIP graphs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5|mixed]
+                       [--no-also | --only KEY,...] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -556,6 +559,8 @@ def main():
                     help="prefill keys per workgroup for long query tiles (0: no split; "
                          "default: chosen from the workload)")
     ap.add_argument("--no-also", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated keys of the 'also' entries to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run plain device copies of this size (a known-traffic kernel "
@@ -611,9 +616,10 @@ def main():
     torch.cuda.empty_cache()
 
     also = {}
+    only = set(args.only.split(",")) if args.only else None
     if not args.no_also:
         for name in ("c4", "c5", "c3", "mixed"):
-            if name == args.workload:
+            if name == args.workload or (only and name not in only):
                 continue
             try:
                 r = Runner(name)
@@ -623,6 +629,8 @@ def main():
             except Exception as e:  # a workload whose kernel is missing is reported as such
                 also[name] = {"error": f"{type(e).__name__}: {e}"}
         for name in ("c2", "c3", "mixed"):
+            if only and f"norm_rope_store_{name}" not in only:
+                continue
             try:
                 also[f"norm_rope_store_{name}"] = norm_rope_store(name, max(5, args.steps // 2))
                 torch.cuda.empty_cache()
@@ -630,6 +638,8 @@ def main():
                 also[f"norm_rope_store_{name}"] = {"error": f"{type(e).__name__}: {e}"}
         for key, batch, fused in (("c2_graph28", None, False), ("c2_b4_graph28", 4, False),
                                   ("c2_graph28_fused_rope", None, True)):
+            if only and key not in only:
+                continue
             try:
                 also[key] = graph_decode("c2", 28, steps=max(5, args.steps // 2), batch=batch,
                                          fused=fused)
