@@ -24,10 +24,15 @@
  *   All work is enqueued on `stream` (may be 0 for the null stream); launch
  *   shapes depend only on host arguments, so calls can be captured in a HIP
  *   graph.
- * - KV cache layout (one layer's slice of the engine pool [Intro §11.5]):
- *   k_cache, v_cache are contiguous [num_blocks, block_size, num_kv_heads,
- *   head_dim] arrays of `dtype`.  Slot s is block s / block_size, offset
- *   s % block_size [Intro §9.2].
+ * - KV cache layout: k_cache, v_cache are contiguous arrays of `dtype`, one
+ *   layer's slice of the engine pool, in one of two layouts chosen by
+ *   `cache_layout`:
+ *     PA_CACHE_BSHD  [num_blocks, block_size, num_kv_heads, head_dim], the
+ *                    nano-vLLM pool [Intro §11.5]: a slot's heads are adjacent;
+ *     PA_CACHE_BHSD  [num_blocks, num_kv_heads, block_size, head_dim], the
+ *                    Pico-vLLM pool [Pico #6]: a head's slots within a block
+ *                    are adjacent.
+ *   Slot s is block s / block_size, offset s % block_size [Intro §9.2].
  * - dtype: PA_DTYPE_F32 or PA_DTYPE_BF16.  q, k, v, qkv, q_out, the norm
  *   weights, caches and out all share it.  Arithmetic is fp32 throughout; outputs are rounded to `dtype`
  *   (round to nearest even for bf16).
@@ -44,6 +49,9 @@
  *   Documented sentinels: slot -1 (no write), block-table entries past a
  *   sequence's ceil(len / block_size) blocks (never read, so -1 padding is
  *   legal), context_len 0 (output zeros).
+ * - cache_layout: PA_CACHE_BSHD or PA_CACHE_BHSD (anything else:
+ *   PA_ERR_UNSUPPORTED); the same value must be used by every call that
+ *   touches one cache.
  * - Return value: PA_OK, or a negative PA_ERR_* code.  Argument checks run on
  *   the host before any launch; a failed launch returns PA_ERR_LAUNCH.
  *   pa_strerror() names a code.
@@ -70,6 +78,8 @@ enum pa_status {
 
 enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
 
+enum pa_cache_layout { PA_CACHE_BSHD = 0, PA_CACHE_BHSD = 1 };
+
 /* Library version as major * 10000 + minor * 100 + patch. */
 int pa_version(void);
 
@@ -80,16 +90,18 @@ const char* pa_strerror(int status);
  * pa_store_kv -- write this step's K and V rows into the paged cache.
  *
  * Defined by [Intro §13.1] and the store of [Pico #6]: for each new token i
- * with s = slot_mapping[i] != -1, copy k[i, h, :] to
- * k_cache[s / block_size, s % block_size, h, :] for every kv head h, and the
- * same for v.  A slot of -1 is a padding row [Intro §13.5] and writes nothing.
- * The copy is bitwise (NaN payloads, signed zeros survive).
+ * with s = slot_mapping[i] != -1, copy k[i, h, :] to the row of kv head h at
+ * slot s of k_cache (k_cache[s / block_size, s % block_size, h, :] in
+ * PA_CACHE_BSHD) for every kv head h, and the same for v.  A slot of -1 is a
+ * padding row [Intro §13.5] and writes nothing.  The copy is bitwise (NaN
+ * payloads, signed zeros survive).
  *
  *   k, v               [num_tokens, num_kv_heads, head_dim], token strides
  *                      k_tok_stride / v_tok_stride and head strides
  *                      k_head_stride / v_head_stride (elements, may describe a
  *                      view into a fused QKV buffer [Pico #6, pitfall 1]).
- *   k_cache, v_cache   as in the conventions; num_blocks physical blocks.
+ *   k_cache, v_cache   as in the conventions; num_blocks physical blocks, laid
+ *                      out as cache_layout says.
  *   slot_mapping       int32 [num_tokens]; unique slots in
  *                      [0, num_blocks * block_size), or -1.
  * num_tokens == 0 is a no-op.  Slots must not repeat within a call (which
@@ -98,8 +110,8 @@ const char* pa_strerror(int status);
 int pa_store_kv(const void* k, const void* v, int64_t k_tok_stride, int64_t k_head_stride,
                 int64_t v_tok_stride, int64_t v_head_stride, void* k_cache, void* v_cache,
                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
-                int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
-                hipStream_t stream);
+                int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                int32_t dtype, hipStream_t stream);
 
 /*
  * pa_qk_norm_rope_store -- per-head q/k RMSNorm, rotary position embedding,
@@ -141,8 +153,8 @@ int pa_qk_norm_rope_store(const void* qkv, int64_t qkv_tok_stride, const void* q
                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, float eps, double rope_theta,
                           void* q_out, int64_t q_out_tok_stride, void* k_cache, void* v_cache,
-                          int32_t block_size, int64_t num_blocks, int32_t dtype,
-                          hipStream_t stream);
+                          int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                          int32_t dtype, hipStream_t stream);
 
 /*
  * pa_decode_workspace_size -- host-only helper for pa_decode.
@@ -188,8 +200,9 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
               const void* v_cache, const int32_t* block_table, int64_t block_table_stride,
               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-              int32_t max_context_len, int32_t partition_tokens, float scale, void* workspace,
-              size_t workspace_bytes, int32_t dtype, hipStream_t stream);
+              int32_t cache_layout, int32_t max_context_len, int32_t partition_tokens,
+              float scale, void* workspace, size_t workspace_bytes, int32_t dtype,
+              hipStream_t stream);
 
 /*
  * pa_decode_reduce -- merge the splits written by pa_decode.
@@ -274,10 +287,11 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
                       const int32_t* cu_seqlens_k, const int32_t* block_table,
                       int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t block_size, int64_t num_blocks, int32_t max_seqlen_q,
-                      int32_t max_seqlen_k, float scale, int32_t split_keys, void* workspace,
-                      size_t workspace_bytes, void* out, int64_t out_tok_stride,
-                      int64_t out_head_stride, int32_t dtype, hipStream_t stream);
+                      int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                      int32_t split_keys, void* workspace, size_t workspace_bytes, void* out,
+                      int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,9 @@ PA_ERR_WORKSPACE = -3
 PA_ERR_LAUNCH = -4
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
+PA_CACHE_BSHD = 0   # [num_blocks, block_size, num_kv_heads, head_dim]
+PA_CACHE_BHSD = 1   # [num_blocks, num_kv_heads, block_size, head_dim]
+LAYOUTS = {"bshd": PA_CACHE_BSHD, "bhsd": PA_CACHE_BHSD}
 
 EXPORTS = (
     "pa_version",
@@ -56,16 +59,17 @@ def _load():
     lib.pa_strerror.argtypes = [ctypes.c_int]
     lib.pa_store_kv.restype = ctypes.c_int
     lib.pa_store_kv.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, i32, i32, i32, i32, i64,
-                                i32, vp]
+                                i32, i32, vp]
     lib.pa_qk_norm_rope_store.restype = ctypes.c_int
     lib.pa_qk_norm_rope_store.argtypes = [vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, f32,
-                                          ctypes.c_double, vp, i64, vp, vp, i32, i64, i32, vp]
+                                          ctypes.c_double, vp, i64, vp, vp, i32, i64, i32, i32,
+                                          vp]
     lib.pa_decode_workspace_size.restype = ctypes.c_int
     lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz),
                                              ctypes.POINTER(i32)]
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, i64,
-                              i32, i32, f32, vp, sz, i32, vp]
+                              i32, i32, i32, f32, vp, sz, i32, vp]
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp, sz, vp, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp]
     lib.pa_prefill_workspace_size.restype = ctypes.c_int
@@ -73,8 +77,8 @@ def _load():
                                               ctypes.POINTER(sz), ctypes.POINTER(i32)]
     lib.pa_prefill_varlen.restype = ctypes.c_int
     lib.pa_prefill_varlen.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
-                                      i32, i32, i64, i32, i32, f32, i32, vp, sz, vp, i64, i64,
-                                      i32, vp]
+                                      i32, i32, i64, i32, i32, i32, f32, i32, vp, sz, vp, i64,
+                                      i64, i32, vp]
     return lib
 
 
@@ -121,31 +125,42 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
-    """Store this step's K/V rows ``[T, Hkv, d]`` into ``[NB, bs, Hkv, d]`` caches."""
-    nb, bs, hkv, d = k_cache.shape
+def _cache_shape(cache, layout):
+    """``(num_blocks, block_size, num_kv_heads, head_dim, layout code)`` of a cache tensor:
+    ``[NB, bs, Hkv, d]`` for layout "bshd", ``[NB, Hkv, bs, d]`` for "bhsd"."""
+    code = LAYOUTS[layout]
+    if code == PA_CACHE_BHSD:
+        nb, hkv, bs, d = cache.shape
+    else:
+        nb, bs, hkv, d = cache.shape
+    return nb, bs, hkv, d, code
+
+
+def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None, layout="bshd") -> None:
+    """Store this step's K/V rows ``[T, Hkv, d]`` into the paged caches."""
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
     assert k.stride(-1) == 1 and v.stride(-1) == 1, "innermost stride must be 1"
     _check("pa_store_kv", library().pa_store_kv(
         _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1), _ptr(k_cache),
-        _ptr(v_cache), _ptr(slot_mapping), slot_mapping.shape[0], hkv, d, bs, nb,
+        _ptr(v_cache), _ptr(slot_mapping), slot_mapping.shape[0], hkv, d, bs, nb, lay,
         _dtype_code(k_cache), _stream(stream)))
 
 
 def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, positions, slot_mapping,
                           num_q_heads, num_kv_heads, eps, rope_theta, q_out, k_cache, v_cache,
-                          stream=None) -> None:
+                          stream=None, layout="bshd") -> None:
     """Per-head q/k RMSNorm + RoPE of ``qkv [T, (Hq + 2 Hkv) d]``; writes ``q_out [T, Hq, d]``
-    and stores rotated K and raw V at ``slot_mapping`` in ``[NB, bs, Hkv, d]`` caches.
+    and stores rotated K and raw V at ``slot_mapping`` in the paged caches.
     Both norm weights ``None``: rotation only."""
-    nb, bs, hkv, d = k_cache.shape
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
     assert hkv == num_kv_heads, "cache head count differs from num_kv_heads"
     assert qkv.stride(-1) == 1 and q_out.stride(-1) == 1, "innermost stride must be 1"
     assert q_out.dim() == 3 and q_out.stride(1) == d, "q_out must be [T, Hq, d] with head stride d"
     _check("pa_qk_norm_rope_store", library().pa_qk_norm_rope_store(
         _ptr(qkv), qkv.stride(0), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions),
         _ptr(slot_mapping), qkv.shape[0], num_q_heads, num_kv_heads, d, eps, rope_theta,
-        _ptr(q_out), q_out.stride(0), _ptr(k_cache), _ptr(v_cache), bs, nb, _dtype_code(qkv),
-        _stream(stream)))
+        _ptr(q_out), q_out.stride(0), _ptr(k_cache), _ptr(v_cache), bs, nb, lay,
+        _dtype_code(qkv), _stream(stream)))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
@@ -160,13 +175,13 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
 
 
 def pa_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len, partition_tokens,
-              scale, workspace, stream=None) -> None:
+              scale, workspace, stream=None, layout="bshd") -> None:
     """Partition pass: ``q [B, Hq, d]``; fills ``workspace`` (a float32 device tensor)."""
-    nb, bs, hkv, d = k_cache.shape
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
     b, hq, _ = q.shape
     _check("pa_decode", library().pa_decode(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        block_table.stride(0), _ptr(context_lens), b, hq, hkv, d, bs, nb, max_context_len,
+        block_table.stride(0), _ptr(context_lens), b, hq, hkv, d, bs, nb, lay, max_context_len,
         partition_tokens, scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _dtype_code(k_cache), _stream(stream)))
 
@@ -194,16 +209,16 @@ def pa_prefill_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head
 
 def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
                       max_seqlen_q, max_seqlen_k, scale, out, workspace, split_keys=0,
-                      stream=None) -> None:
+                      stream=None, layout="bshd") -> None:
     """Causal varlen prefill: ``q, out [Tq, Hq, d]``; K/V read from the paged caches.
     ``workspace``: a device tensor of at least pa_prefill_workspace_size bytes for the
     same sizes and ``split_keys`` (> 0 cuts long query tiles' key loops)."""
-    nb, bs, hkv, d = k_cache.shape
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
     tq, hq, _ = q.shape
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("pa_prefill_varlen", library().pa_prefill_varlen(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
         _ptr(cu_seqlens_k), _ptr(block_table), block_table.stride(0), cu_seqlens_q.shape[0] - 1,
-        tq, hq, hkv, d, bs, nb, max_seqlen_q, max_seqlen_k, scale, split_keys,
+        tq, hq, hkv, d, bs, nb, lay, max_seqlen_q, max_seqlen_k, scale, split_keys,
         _ptr(workspace), ws_bytes, _ptr(out), out.stride(0), out.stride(1), _dtype_code(q),
         _stream(stream)))

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 constexpr int64_t kPrefillMaxTableEntries = 8192;  // 32 KB of LDS beside the K/V tile buffers
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -29,6 +29,13 @@ bool group_ok(int32_t hq, int32_t hkv) {
 
 int launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+bool layout_ok(int32_t l) { return l == PA_CACHE_BSHD || l == PA_CACHE_BHSD; }
+
+pa::CacheGeom geom_of(int32_t layout, int32_t num_kv_heads, int32_t block_size,
+                      int32_t head_dim) {
+  return pa::cache_geom(layout == PA_CACHE_BHSD, num_kv_heads, block_size, head_dim);
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,10 +56,10 @@ const char* pa_strerror(int status) {
 int pa_store_kv(const void* k, const void* v, int64_t k_tok_stride, int64_t k_head_stride,
                 int64_t v_tok_stride, int64_t v_head_stride, void* k_cache, void* v_cache,
                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
-                int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
-                hipStream_t stream) {
+                int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                int32_t dtype, hipStream_t stream) {
   const int eb = elt_bytes(dtype);
-  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
   if (k_tok_stride < 0 || k_head_stride < 0 || v_tok_stride < 0 || v_head_stride < 0)
@@ -64,7 +71,8 @@ int pa_store_kv(const void* k, const void* v, int64_t k_tok_stride, int64_t k_he
   if (int64_t{num_tokens} * 2 * num_kv_heads * head_dim >= (int64_t{1} << 31))
     return PA_ERR_UNSUPPORTED;
   pa::StoreArgs a{k, v, k_tok_stride, k_head_stride, v_tok_stride, v_head_stride, k_cache,
-                  v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, eb};
+                  v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, eb,
+                  geom_of(cache_layout, num_kv_heads, block_size, head_dim)};
   return launched(pa::launch_store(a, stream));
 }
 
@@ -73,10 +81,10 @@ int pa_qk_norm_rope_store(const void* qkv, int64_t qkv_tok_stride, const void* q
                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, float eps, double rope_theta,
                           void* q_out, int64_t q_out_tok_stride, void* k_cache, void* v_cache,
-                          int32_t block_size, int64_t num_blocks, int32_t dtype,
-                          hipStream_t stream) {
+                          int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                          int32_t dtype, hipStream_t stream) {
   const int eb = elt_bytes(dtype);
-  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
@@ -99,7 +107,8 @@ int pa_qk_norm_rope_store(const void* qkv, int64_t qkv_tok_stride, const void* q
     return PA_ERR_UNSUPPORTED;
   pa::RopeArgs a{qkv, qkv_tok_stride, q_norm_weight, k_norm_weight, positions, slot_mapping,
                  num_tokens, num_q_heads, num_kv_heads, head_dim, eps, rope_theta, q_out,
-                 q_out_tok_stride, k_cache, v_cache, eb};
+                 q_out_tok_stride, k_cache, v_cache, block_size, eb,
+                 geom_of(cache_layout, num_kv_heads, block_size, head_dim)};
   return launched(pa::launch_norm_rope_store(a, stream));
 }
 
@@ -121,10 +130,11 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
               const void* v_cache, const int32_t* block_table, int64_t block_table_stride,
               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-              int32_t max_context_len, int32_t partition_tokens, float scale, void* workspace,
-              size_t workspace_bytes, int32_t dtype, hipStream_t stream) {
+              int32_t cache_layout, int32_t max_context_len, int32_t partition_tokens,
+              float scale, void* workspace, size_t workspace_bytes, int32_t dtype,
+              hipStream_t stream) {
   const int eb = elt_bytes(dtype);
-  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_context_len < 0 || num_blocks <= 0 || block_size <= 0)
     return PA_ERR_INVALID_ARG;
   if (!group_ok(num_q_heads, num_kv_heads)) {
@@ -133,7 +143,9 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
     return PA_ERR_UNSUPPORTED;
   }
   if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
-  if (num_blocks > (int64_t{1} << 40)) return PA_ERR_UNSUPPORTED;
+  if (num_blocks > (int64_t{1} << 32) ||
+      int64_t{block_size} * num_kv_heads * head_dim > int64_t{UINT32_MAX})
+    return PA_ERR_UNSUPPORTED;  // 32-bit block ids and block strides
   if (q_seq_stride < 0 || q_head_stride < 0 || block_table_stride < 0) return PA_ERR_INVALID_ARG;
   if (!(scale == scale)) return PA_ERR_INVALID_ARG;  // NaN scale
   size_t need = 0;
@@ -154,8 +166,8 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
   pa::DecodeArgs a{q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
                    block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
                    head_dim, block_size, max_context_len, partition_tokens, splits, scale, ws,
-                   ws + acc_elems,
-                   dtype == PA_DTYPE_BF16};
+                   ws + acc_elems, dtype == PA_DTYPE_BF16,
+                   geom_of(cache_layout, num_kv_heads, block_size, head_dim)};
   return launched(pa::launch_decode(a, stream));
 }
 
@@ -238,12 +250,13 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
                       const int32_t* cu_seqlens_k, const int32_t* block_table,
                       int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t block_size, int64_t num_blocks, int32_t max_seqlen_q,
-                      int32_t max_seqlen_k, float scale, int32_t split_keys, void* workspace,
-                      size_t workspace_bytes, void* out, int64_t out_tok_stride,
-                      int64_t out_head_stride, int32_t dtype, hipStream_t stream) {
+                      int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                      int32_t split_keys, void* workspace, size_t workspace_bytes, void* out,
+                      int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
+                      hipStream_t stream) {
   const int eb = elt_bytes(dtype);
-  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_blocks <= 0 ||
       block_size <= 0)
     return PA_ERR_INVALID_ARG;
@@ -293,7 +306,8 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
                     reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.merges_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off),
-                    out, out_tok_stride, out_head_stride};
+                    out, out_tok_stride, out_head_stride,
+                    geom_of(cache_layout, num_kv_heads, block_size, head_dim)};
   return launched(pa::launch_prefill(a, stream));
 }
 

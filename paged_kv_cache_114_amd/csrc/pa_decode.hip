@@ -53,7 +53,8 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     const int32_t* __restrict__ block_table, int64_t bt_stride,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_kv_heads,
     int32_t bs_log2, int32_t bt_entries, int32_t partition_tokens, int32_t num_splits,
-    float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t block_stride,
+    int32_t slot_stride, int64_t head_stride) {
   using S = DecodeShape<T, D, G>;
   constexpr int kE = S::kE, kR = S::kR, kTpl = S::kTpl, kU = S::kU, kTile = S::kTile;
   extern __shared__ int32_t bt_lds[];
@@ -107,9 +108,8 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     for (int e = 0; e < kE; ++e) acc[i][e] = 0.f;
   }
 
-  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;
-  const T* kbase = k_cache + static_cast<int64_t>(g) * D + col * kE;
-  const T* vbase = v_cache + static_cast<int64_t>(g) * D + col * kE;
+  const T* kbase = k_cache + g * head_stride + col * kE;
+  const T* vbase = v_cache + g * head_stride + col * kE;
   const int bs_mask = (1 << bs_log2) - 1;
 
   // Loads of tile n+1 are issued before tile n is consumed, so a wave never
@@ -121,8 +121,10 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int j = min(tb + u * kTpl + row, t1 - 1);
-      const int64_t blk = bt_lds[(j >> bs_log2) - first_blk];
-      const int64_t off = ((blk << bs_log2) + (j & bs_mask)) * slot_stride;
+      // one 32 x 32 -> 64-bit multiply: block ids and the block stride fit 32 bits
+      const uint32_t blk = bt_lds[(j >> bs_log2) - first_blk];
+      const uint64_t off = static_cast<uint64_t>(blk) * block_stride +
+                           static_cast<uint32_t>(j & bs_mask) * static_cast<uint32_t>(slot_stride);
       kr[u] = load16(kbase + off);
       vr[u] = load16(vbase + off);
     }
@@ -299,8 +301,9 @@ hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
                      a.q_seq_stride, a.q_head_stride, static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_table, a.block_table_stride,
                      a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, bt_entries,
-                     a.partition_tokens, a.num_splits,
-                     a.scale * kLog2e, a.ws_acc, a.ws_ml);
+                     a.partition_tokens, a.num_splits, a.scale * kLog2e, a.ws_acc, a.ws_ml,
+                     static_cast<uint32_t>(a.geom.block), static_cast<int32_t>(a.geom.slot),
+                     a.geom.head);
   return hipGetLastError();
 }
 

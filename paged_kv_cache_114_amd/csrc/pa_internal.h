@@ -6,6 +6,18 @@
 
 namespace pa {
 
+// Where element (block, slot offset, kv head, 0) of a cache sits: strides in
+// elements.  Block-major slots then heads ([blocks, block_size, heads, dim])
+// or block-major heads then slots ([blocks, heads, block_size, dim]).
+struct CacheGeom {
+  int64_t block, slot, head;
+};
+inline CacheGeom cache_geom(bool heads_outer, int64_t num_kv_heads, int64_t block_size,
+                            int64_t head_dim) {
+  if (heads_outer) return {num_kv_heads * block_size * head_dim, head_dim, block_size * head_dim};
+  return {block_size * num_kv_heads * head_dim, num_kv_heads * head_dim, head_dim};
+}
+
 struct StoreArgs {
   const void* k;
   const void* v;
@@ -15,6 +27,7 @@ struct StoreArgs {
   const int32_t* slot_mapping;
   int32_t num_tokens, num_kv_heads, head_dim, block_size;
   int32_t elt_bytes;  // 2 (bf16) or 4 (fp32)
+  CacheGeom geom;
 };
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 
@@ -32,6 +45,7 @@ struct DecodeArgs {
   float* ws_acc;  // [B, Hq, S, D]
   float* ws_ml;   // [B, Hq, S, 2]
   bool bf16;
+  CacheGeom geom;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
@@ -66,6 +80,7 @@ struct PrefillArgs {
   float* ws_ml;                    // [S, total_q, Hq, 2]
   void* out;
   int64_t out_tok_stride, out_head_stride;
+  CacheGeom geom;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
@@ -83,7 +98,9 @@ struct RopeArgs {
   int64_t q_out_tok_stride;
   void* k_cache;
   void* v_cache;
+  int32_t block_size;
   int32_t elt_bytes;
+  CacheGeom geom;
 };
 hipError_t launch_norm_rope_store(const RopeArgs& a, hipStream_t stream);
 

@@ -132,7 +132,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     int32_t bs_log2, float scale_log2, int32_t split_tiles, uint32_t* __restrict__ tickets,
     const int2* __restrict__ items, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int32_t total_q, uint16_t* __restrict__ out, int64_t out_tok_stride,
-    int64_t out_head_stride) {
+    int64_t out_head_stride, int64_t block_stride, int64_t slot_stride, int64_t head_stride) {
   using S = PrefillShape<D, G>;
   // Two K/V tile buffers, row-major [key][dim], each row's 16-byte chunks
   // XOR-swizzled (k_swizzle / v_swizzle) so the MFMA operand reads are free
@@ -174,7 +174,6 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     const int chunk = db * 4 + 2 * (col / 16) + j4 / 2;
     v_off[db] = key * D + 8 * (chunk ^ v_swizzle<D>(key)) + 4 * (j4 % 2);
   }
-  const int64_t slot_stride = static_cast<int64_t>(num_kv_heads) * D;  // elements per slot
   const int bs_mask = (1 << bs_log2) - 1;
   // When a block holds at least a tile (64 tokens), the 64 rows of a tile are
   // consecutive slots of one block, so a DMA source is one wave-uniform base
@@ -275,8 +274,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     if (tile_in_block && kt0 + kBN - 1 <= last_pos) {
       const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(kt0 >> bs_log2) - first_blk]);
       const int64_t tile_off =
-          ((static_cast<int64_t>(blk) << bs_log2) + (kt0 & bs_mask)) * slot_stride +
-          static_cast<int64_t>(g) * D;
+          blk * block_stride + (kt0 & bs_mask) * slot_stride + g * head_stride;
       // a buffer resource over the tile's first row: scalar base, 32-bit lane offsets
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(cache + tile_off), 0, 0x7fffffff, kBufferFlags);
@@ -299,8 +297,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
         const int r0 = min(kt0 + piece * S::kRowsPerDma, last_pos);
         const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(r0 >> bs_log2) - first_blk]);
         const int64_t row_off =
-            ((static_cast<int64_t>(blk) << bs_log2) + (r0 & bs_mask)) * slot_stride +
-            static_cast<int64_t>(g) * D;
+            blk * block_stride + (r0 & bs_mask) * slot_stride + g * head_stride;
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(cache + row_off), 0, 0x7fffffff, kBufferFlags);
         const int lane_row = lane / S::kChunks;
@@ -759,7 +756,7 @@ hipError_t run(const PrefillArgs& a, hipStream_t stream) {
                      a.cu_seqlens_q, a.cu_seqlens_k, a.block_table, a.block_table_stride,
                      a.num_kv_heads, bs_log2, a.scale * kLog2e, split_tiles, a.tickets, a.items,
                      a.ws_acc, a.ws_ml, a.total_q, static_cast<uint16_t*>(a.out),
-                     a.out_tok_stride, a.out_head_stride);
+                     a.out_tok_stride, a.out_head_stride, a.geom.block, a.geom.slot, a.geom.head);
   err = hipGetLastError();
   if (err != hipSuccess || a.num_splits == 1) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(4 * cus), dim3(256), 0, stream,

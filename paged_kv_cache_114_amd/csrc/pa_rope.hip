@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kRopeWaves* kWave) void norm_rope_store_kernel(
     const char* __restrict__ k_weight, const int32_t* __restrict__ positions,
     const int32_t* __restrict__ slot_mapping, int32_t num_items, int32_t passes,
     int32_t num_q_heads, int32_t num_kv_heads, float eps, double freq_ratio, char* q_out,
-    int64_t q_out_tok_b, char* k_cache, char* v_cache, int64_t cache_row_b) {
+    int64_t q_out_tok_b, char* k_cache, char* v_cache, int32_t bs_log2, int64_t block_b,
+    int64_t slot_b, int64_t cache_head_b) {
   using E = Eight<T>;
   constexpr int kEb = Elt<T>::kBytes;
   constexpr int kPairs = D / 2;
@@ -210,8 +211,8 @@ __global__ __launch_bounds__(kRopeWaves* kWave) void norm_rope_store_kernel(
         dst = q_out + tok * q_out_tok_b + static_cast<int64_t>(hs) * kHeadBytes;
       } else {
         const int kv = is_v ? hs - num_q_heads - num_kv_heads : hs - num_q_heads;
-        dst = (is_v ? v_cache : k_cache) + slot * cache_row_b +
-              static_cast<int64_t>(kv) * kHeadBytes;
+        dst = (is_v ? v_cache : k_cache) + (slot >> bs_log2) * block_b +
+              (slot & ((1 << bs_log2) - 1)) * slot_b + kv * cache_head_b;
       }
       uint4 oa[E::kWords], ob[E::kWords];
       if (is_v) {  // V is copied bit for bit
@@ -256,7 +257,8 @@ hipError_t run(const RopeArgs& a, hipStream_t stream) {
                      a.num_q_heads, a.num_kv_heads, a.eps, freq_ratio,
                      static_cast<char*>(a.q_out), a.q_out_tok_stride * eb,
                      static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache),
-                     int64_t{a.num_kv_heads} * a.head_dim * eb);
+                     __builtin_ctz(static_cast<unsigned>(a.block_size)), a.geom.block * eb,
+                     a.geom.slot * eb, a.geom.head * eb);
   return hipGetLastError();
 }
 

@@ -6,8 +6,10 @@
 // strided view (token and head strides), the point of [Pico #6, pitfall 1].
 //
 // One wave moves one (token, K or V) row: num_kv_heads * head_dim elements,
-// read as W-sized words.  The slot is loaded once per row and is uniform over
-// the wave (a padding row is skipped whole).  Lane l takes words l, l + 64,
+// read as W-sized words and written to the slot's head rows (adjacent in the
+// slots-then-heads layout, block_size rows apart in the heads-then-slots
+// one).  The slot is loaded once per row and is uniform over the wave (a
+// padding row is skipped whole).  Lane l takes words l, l + 64,
 // ...; each lane issues all of its loads before its first store, so a wave
 // keeps the whole row in flight.  A word's head is word >> hw_log2
 // (head_dim * element size / sizeof(W) is a power of two).
@@ -27,9 +29,10 @@ __global__ __launch_bounds__(kStoreWaves* kWave) void store_kernel(
     const char* __restrict__ k, const char* __restrict__ v, int64_t k_tok_b, int64_t k_head_b,
     int64_t v_tok_b, int64_t v_head_b, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const int32_t* __restrict__ slot_mapping, int32_t rows, int32_t words_per_row,
-    int32_t hw_log2, int64_t row_bytes, int64_t head_bytes) {
+    int32_t hw_log2, int32_t bs_log2, int64_t block_b, int64_t slot_b, int64_t cache_head_b) {
   const int lane = threadIdx.x % kWave;
   const int hw_mask = (1 << hw_log2) - 1;
+  const int bs_mask = (1 << bs_log2) - 1;
   for (int r = blockIdx.x * kStoreWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
        r < rows; r += gridDim.x * kStoreWaves) {
     const int tok = r >> 1;
@@ -38,7 +41,8 @@ __global__ __launch_bounds__(kStoreWaves* kWave) void store_kernel(
     if (slot < 0) continue;  // -1: padding row, nothing to write
     const char* src = is_v ? v + tok * v_tok_b : k + tok * k_tok_b;
     const int64_t head_b = is_v ? v_head_b : k_head_b;
-    char* dst = (is_v ? v_cache : k_cache) + static_cast<int64_t>(slot) * row_bytes;
+    char* dst =
+        (is_v ? v_cache : k_cache) + (slot >> bs_log2) * block_b + (slot & bs_mask) * slot_b;
     for (int w0 = 0; w0 < words_per_row; w0 += kStoreUnroll * kWave) {
       // No lane branches: a lane past the row re-reads its last word and writes
       // the same value back, so the loads issue back to back and the wave waits
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(kStoreWaves* kWave) void store_kernel(
 #pragma unroll
       for (int u = 0; u < kStoreUnroll; ++u) {
         const int w = min(w0 + u * kWave + lane, words_per_row - 1);
-        *reinterpret_cast<W*>(dst + (w >> hw_log2) * head_bytes +
+        *reinterpret_cast<W*>(dst + (w >> hw_log2) * cache_head_b +
                               (w & hw_mask) * static_cast<int64_t>(sizeof(W))) = val[u];
       }
     }
@@ -76,8 +80,8 @@ hipError_t run(const StoreArgs& a, hipStream_t stream) {
                      a.k_tok_stride * eb, a.k_head_stride * eb, a.v_tok_stride * eb,
                      a.v_head_stride * eb, static_cast<char*>(a.k_cache),
                      static_cast<char*>(a.v_cache), a.slot_mapping, static_cast<int32_t>(rows),
-                     words_per_row, hw_log2, static_cast<int64_t>(a.num_kv_heads) * a.head_dim * eb,
-                     static_cast<int64_t>(a.head_dim) * eb);
+                     words_per_row, hw_log2, __builtin_ctz(static_cast<unsigned>(a.block_size)),
+                     a.geom.block * eb, a.geom.slot * eb, a.geom.head * eb);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert pa.version() == 100
+    assert pa.version() == 200
     assert pa.strerror(pa.PA_OK) == "ok"
     for code in (pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED, pa.PA_ERR_WORKSPACE,
                  pa.PA_ERR_LAUNCH):
@@ -59,12 +59,12 @@ def test_workspace_size_formula():
 
 def store(**kw):
     args = dict(k=NULL, v=NULL, kts=1024, khs=128, vts=1024, vhs=128, kc=NULL, vc=NULL, slots=NULL,
-                t=4, hkv=8, d=128, bs=256, nb=10, dtype=BF16)
+                t=4, hkv=8, d=128, bs=256, nb=10, lay=0, dtype=BF16)
     args.update(kw)
     return pa.library().pa_store_kv(args["k"], args["v"], args["kts"], args["khs"], args["vts"],
                                     args["vhs"], args["kc"], args["vc"], args["slots"], args["t"],
-                                    args["hkv"], args["d"], args["bs"], args["nb"], args["dtype"],
-                                    NULL)
+                                    args["hkv"], args["d"], args["bs"], args["nb"], args["lay"],
+                                    args["dtype"], NULL)
 
 
 def test_store_validation():
@@ -77,17 +77,19 @@ def test_store_validation():
     assert store(t=-1) == pa.PA_ERR_INVALID_ARG
     assert store(kts=-8) == pa.PA_ERR_INVALID_ARG
     assert store(hkv=0) == pa.PA_ERR_INVALID_ARG
+    assert store(lay=2) == pa.PA_ERR_UNSUPPORTED
+    assert store(lay=1) == pa.PA_ERR_INVALID_ARG                # valid layout, null pointers
 
 
 def decode(**kw):
     args = dict(q=NULL, qs=2048, qh=128, kc=NULL, vc=NULL, bt=NULL, bts=16, cl=NULL, b=4, hq=16,
-                hkv=8, d=128, bs=256, nb=100, maxctx=4096, p=1024, scale=0.088, ws=NULL,
+                hkv=8, d=128, bs=256, nb=100, lay=0, maxctx=4096, p=1024, scale=0.088, ws=NULL,
                 wsb=1 << 30, dtype=BF16)
     args.update(kw)
     a = args
     return pa.library().pa_decode(a["q"], a["qs"], a["qh"], a["kc"], a["vc"], a["bt"], a["bts"],
                                   a["cl"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
-                                  a["maxctx"], a["p"], a["scale"], a["ws"], a["wsb"], a["dtype"],
+                                  a["lay"], a["maxctx"], a["p"], a["scale"], a["ws"], a["wsb"], a["dtype"],
                                   NULL)
 
 
@@ -103,6 +105,8 @@ def test_decode_validation():
     assert decode(dtype=3) == pa.PA_ERR_UNSUPPORTED
     assert decode(scale=float("nan")) == pa.PA_ERR_INVALID_ARG
     assert decode(b=-1) == pa.PA_ERR_INVALID_ARG
+    assert decode(lay=-1) == pa.PA_ERR_UNSUPPORTED
+    assert decode(nb=(1 << 32) + 1) == pa.PA_ERR_UNSUPPORTED     # 32-bit block ids
     # a too-small workspace is caught before any pointer is used
     fake = ctypes.c_void_p(256)
     assert decode(q=fake, kc=fake, vc=fake, bt=fake, cl=fake, ws=fake, wsb=100) == \
@@ -134,13 +138,14 @@ def test_reduce_validation():
 
 def prefill(**kw):
     args = dict(q=NULL, qt=2048, qh=128, kc=NULL, vc=NULL, cq=NULL, ck=NULL, bt=NULL, bts=8, b=8,
-                tq=6000, hq=16, hkv=8, d=128, bs=256, nb=64, mq=2048, mk=2048, scale=0.088,
+                tq=6000, hq=16, hkv=8, d=128, bs=256, nb=64, lay=0, mq=2048, mk=2048, scale=0.088,
                 sk=0, ws=NULL, wsb=0, out=NULL, ot=2048, oh=128, dtype=BF16)
     args.update(kw)
     a = args
     return pa.library().pa_prefill_varlen(a["q"], a["qt"], a["qh"], a["kc"], a["vc"], a["cq"],
                                           a["ck"], a["bt"], a["bts"], a["b"], a["tq"], a["hq"],
-                                          a["hkv"], a["d"], a["bs"], a["nb"], a["mq"], a["mk"],
+                                          a["hkv"], a["d"], a["bs"], a["nb"], a["lay"], a["mq"],
+                                          a["mk"],
                                           a["scale"], a["sk"], a["ws"], a["wsb"], a["out"],
                                           a["ot"], a["oh"], a["dtype"], NULL)
 
@@ -157,6 +162,7 @@ def test_prefill_validation():
     assert prefill(scale=-0.5) == pa.PA_ERR_INVALID_ARG
     assert prefill(scale=float("nan")) == pa.PA_ERR_INVALID_ARG
     assert prefill(bs=8, mk=8 * 16384 + 1, mq=100) == pa.PA_ERR_UNSUPPORTED
+    assert prefill(lay=3) == pa.PA_ERR_UNSUPPORTED
 
 
 def test_prefill_workspace_size_formula():
@@ -195,13 +201,13 @@ def test_prefill_split_validation():
 def rope(**kw):
     args = dict(qkv=NULL, qs=4096, qw=NULL, kw=NULL, pos=NULL, slots=NULL, t=4, hq=16, hkv=8,
                 d=128, eps=1e-6, theta=1e6, q=NULL, qos=2048, kc=NULL, vc=NULL, bs=256, nb=10,
-                dtype=BF16)
+                lay=0, dtype=BF16)
     args.update(kw)
     a = args
     return pa.library().pa_qk_norm_rope_store(
         a["qkv"], a["qs"], a["qw"], a["kw"], a["pos"], a["slots"], a["t"], a["hq"], a["hkv"],
         a["d"], a["eps"], a["theta"], a["q"], a["qos"], a["kc"], a["vc"], a["bs"], a["nb"],
-        a["dtype"], NULL)
+        a["lay"], a["dtype"], NULL)
 
 
 def test_norm_rope_store_validation():
@@ -213,6 +219,7 @@ def test_norm_rope_store_validation():
     assert rope(d=96) == pa.PA_ERR_UNSUPPORTED
     assert rope(bs=100) == pa.PA_ERR_UNSUPPORTED
     assert rope(dtype=5) == pa.PA_ERR_UNSUPPORTED
+    assert rope(lay=9) == pa.PA_ERR_UNSUPPORTED
     assert rope(hkv=0) == pa.PA_ERR_INVALID_ARG
     assert rope(qs=4000) == pa.PA_ERR_INVALID_ARG                  # row shorter than Q, K, V
     assert rope(qos=1024) == pa.PA_ERR_INVALID_ARG                 # q_out row too short
