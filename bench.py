@@ -144,15 +144,19 @@ class HipEvents:
 class Runner:
     """Buffers and launches for one workload; times each step with HIP events."""
 
-    def __init__(self, name, partition=None, split_keys=None):
+    def __init__(self, name, partition=None, split_keys=None, layout="bshd", case=None):
         import torch
 
         import paged_kv_cache_114_amd as pa
         import workloads as W
         self.torch, self.pa, self.W = torch, pa, W
         self.name = name
-        self.case = W.FULL_CASES[name]()
+        self.case = W.FULL_CASES[name]() if case is None else case
         self.vals = W.materialize(self.case, "cuda:0")
+        self.layout = layout
+        if layout == "bhsd":  # the pool transposed to [NB, Hkv, bs, d]
+            for key in ("k_cache", "v_cache"):
+                self.vals[key] = self.vals[key].permute(0, 2, 1, 3).contiguous()
         c = self.case
         self.kind = c.kind
         if self.kind == "decode":
@@ -179,11 +183,12 @@ class Runner:
         """One step; events 4k .. 4k+3 bracket store, main kernel and (decode) reduce."""
         pa, v, c = self.pa, self.vals, self.case
         ev.record(4 * k)
-        pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"], v["slot_mapping"])
+        pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"], v["slot_mapping"],
+                       layout=self.layout)
         ev.record(4 * k + 1)
         if self.kind == "decode":
             pa.pa_decode(v["q"], v["k_cache"], v["v_cache"], v["block_table"], v["context_lens"],
-                         c.max_context_len, self.partition, c.scale, self.ws)
+                         c.max_context_len, self.partition, c.scale, self.ws, layout=self.layout)
             ev.record(4 * k + 2)
             pa.pa_decode_reduce(self.ws, v["context_lens"], self.splits, self.partition,
                                 self.out)
@@ -191,7 +196,7 @@ class Runner:
             pa.pa_prefill_varlen(v["q"], v["k_cache"], v["v_cache"], v["cu_seqlens_q"],
                                  v["cu_seqlens_k"], v["block_table"], c.max_seqlen_q,
                                  c.max_context_len, c.scale, self.out, self.ws,
-                                 split_keys=self.split_keys)
+                                 split_keys=self.split_keys, layout=self.layout)
             ev.record(4 * k + 2)
         ev.record(4 * k + 3)
 
@@ -230,7 +235,7 @@ class Runner:
             unique = c.kv_bytes_unique()
             rate = logical / (t["step_ms"] * 1e-3) / 1e9
             kern = logical / (t["main_ms"] * 1e-3) / 1e9
-            out = {"workload": c.name, "kv_GBps_step": round(rate, 1),
+            out = {"workload": c.name, "layout": self.layout, "kv_GBps_step": round(rate, 1),
                    "decode_kernel_GBps": round(kern, 1),
                    "decode_kernel_frac_hbm": round(kern / HBM_PEAK_GBS, 4),
                    "ms_per_step": round(t["step_ms"], 5),
@@ -243,7 +248,7 @@ class Runner:
             return out
         flops = self.prefill_flops()
         tf = flops / (t["main_ms"] * 1e-3) / 1e12
-        return {"workload": c.name, "prefill_TFLOPs_kernel": round(tf, 2),
+        return {"workload": c.name, "layout": self.layout, "prefill_TFLOPs_kernel": round(tf, 2),
                 "frac_bf16_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                 "ms_per_step": round(t["step_ms"], 5), "prefill_kernel_ms": round(t["main_ms"], 5),
                 "gflop": round(flops / 1e9, 3), "split_keys": self.split_keys,
@@ -628,6 +633,24 @@ def main():
                 torch.cuda.empty_cache()
             except Exception as e:  # a workload whose kernel is missing is reported as such
                 also[name] = {"error": f"{type(e).__name__}: {e}"}
+        # the head-major pool, and smaller blocks, on the decode and prefill workloads
+        import workloads as W
+        variants = [("layout_bhsd_c2", "c2", "bhsd", None), ("layout_bhsd_c3", "c3", "bhsd", None)]
+        for bs in (16, 64):
+            for layout in ("bshd", "bhsd"):
+                variants.append((f"bs{bs}_{layout}_c2", "c2", layout,
+                                 W.c2_decode(name=f"c2_decode_b64_bs{bs}", bs=bs)))
+        for key, name, layout, case in variants:
+            if only and key not in only:
+                continue
+            try:
+                r = Runner(name, layout=layout, case=case)
+                also[key] = r.summary(r.run(max(5, args.steps // 2), 3))
+                also[key]["block_size"] = r.case.block_size
+                del r
+                torch.cuda.empty_cache()
+            except Exception as e:
+                also[key] = {"error": f"{type(e).__name__}: {e}"}
         for name in ("c2", "c3", "mixed"):
             if only and f"norm_rope_store_{name}" not in only:
                 continue

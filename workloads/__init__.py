@@ -232,11 +232,11 @@ def c1_tiny_decode() -> Case:
                        dtype="f32", bs=16, pool=8)
 
 
-def c2_decode(batch=64, seed=1142, name="c2_decode_b64") -> Case:
-    """Qwen3-0.6B one-layer decode: contexts uniform in [128, 1024], block 256."""
+def c2_decode(batch=64, seed=1142, name="c2_decode_b64", bs=256) -> Case:
+    """Qwen3-0.6B one-layer decode: contexts uniform in [128, 1024], block 256 (or ``bs``)."""
     rng = np.random.default_rng(seed)
     lengths = rng.integers(128, 1024, size=batch, endpoint=True)
-    return decode_case(name, seed, lengths=lengths)
+    return decode_case(name, seed, lengths=lengths, bs=bs)
 
 
 def _prefill_lengths(rng, nseq, lo, hi, n_cached, cached_choices):
