@@ -205,6 +205,38 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
               hipStream_t stream);
 
 /*
+ * pa_store_decode -- pa_store_kv of one new token per sequence and the
+ * pa_decode partition pass, in one launch.
+ *
+ * The decode step of [Intro §13.1, §13.2] (store this step's K/V, then
+ * attend) for the batch where sequence b has exactly one new token, row b of
+ * k_new / v_new, at position context_lens[b] - 1 and slot slot_mapping[b]
+ * (-1: no store; such a row is a padding row and must have context_lens[b]
+ * = 0).  The cache rows at those slots afterwards hold the new K/V exactly as
+ * pa_store_kv writes them, and the workspace holds exactly what pa_decode
+ * writes after that store (bit for bit); follow with pa_decode_reduce.
+ * slot_mapping[b] must be the slot block_table[b] gives position
+ * context_lens[b] - 1 (the slot the engine computes for it [Intro §11.4]).
+ *
+ *   k_new, v_new   [num_seqs, num_kv_heads, head_dim] of dtype, strides
+ *                  k_tok_stride / k_head_stride and v_tok_stride /
+ *                  v_head_stride (elements, 16-byte aligned rows).
+ *   slot_mapping   int32 [num_seqs].
+ * Every other argument is as for pa_decode; the caches are written, so they
+ * are not const here.
+ */
+int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                    int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                    const int32_t* slot_mapping, const void* q, int64_t q_seq_stride,
+                    int64_t q_head_stride, void* k_cache, void* v_cache,
+                    const int32_t* block_table, int64_t block_table_stride,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t cache_layout, int32_t max_context_len,
+                    int32_t partition_tokens, float scale, void* workspace,
+                    size_t workspace_bytes, int32_t dtype, hipStream_t stream);
+
+/*
  * pa_decode_reduce -- merge the splits written by pa_decode.
  *
  * [Intro §9.5]: with m* = max_s m_s, out = sum_s 2^(m_s - m*) acc_s /

@@ -35,6 +35,7 @@ EXPORTS = (
     "pa_qk_norm_rope_store",
     "pa_decode_workspace_size",
     "pa_decode",
+    "pa_store_decode",
     "pa_decode_reduce",
     "pa_prefill_workspace_size",
     "pa_prefill_varlen",
@@ -70,6 +71,10 @@ def _load():
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, i64,
                               i32, i32, i32, f32, vp, sz, i32, vp]
+    lib.pa_store_decode.restype = ctypes.c_int
+    lib.pa_store_decode.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, i64,
+                                    vp, i32, i32, i32, i32, i32, i64, i32, i32, i32, f32, vp, sz,
+                                    i32, vp]
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp, sz, vp, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp]
     lib.pa_prefill_workspace_size.restype = ctypes.c_int
@@ -184,6 +189,22 @@ def pa_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len, p
         block_table.stride(0), _ptr(context_lens), b, hq, hkv, d, bs, nb, lay, max_context_len,
         partition_tokens, scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_store_decode(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_table, context_lens,
+                    max_context_len, partition_tokens, scale, workspace, stream=None,
+                    layout="bshd") -> None:
+    """Store each sequence's new K/V row (``[B, Hkv, d]``, at position ``context_lens - 1``)
+    through ``slot_mapping`` and run the partition pass, in one launch."""
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    b, hq, _ = q.shape
+    assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"
+    _check("pa_store_decode", library().pa_store_decode(
+        _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1), v_new.stride(0),
+        v_new.stride(1), _ptr(slot_mapping), _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), block_table.stride(0), _ptr(context_lens), b, hq, hkv,
+        d, bs, nb, lay, max_context_len, partition_tokens, scale, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _dtype_code(k_cache), _stream(stream)))
 
 
 def pa_decode_reduce(workspace, context_lens, num_splits, partition_tokens, out,

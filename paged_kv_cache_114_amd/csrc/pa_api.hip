@@ -126,13 +126,23 @@ int pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head
   return PA_OK;
 }
 
-int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const void* k_cache,
-              const void* v_cache, const int32_t* block_table, int64_t block_table_stride,
-              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-              int32_t cache_layout, int32_t max_context_len, int32_t partition_tokens,
-              float scale, void* workspace, size_t workspace_bytes, int32_t dtype,
-              hipStream_t stream) {
+namespace {
+
+struct NewRows {  // the fused store of pa_store_decode (k == nullptr: none)
+  const void* k;
+  const void* v;
+  int64_t k_tok_stride, k_head_stride, v_tok_stride, v_head_stride;
+  const int32_t* slot_mapping;
+};
+
+int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
+                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                  int64_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                  int32_t max_context_len, int32_t partition_tokens, float scale,
+                  void* workspace, size_t workspace_bytes, int32_t dtype, const NewRows& nr,
+                  hipStream_t stream) {
   const int eb = elt_bytes(dtype);
   if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_context_len < 0 || num_blocks <= 0 || block_size <= 0)
@@ -147,6 +157,9 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
       int64_t{block_size} * num_kv_heads * head_dim > int64_t{UINT32_MAX})
     return PA_ERR_UNSUPPORTED;  // 32-bit block ids and block strides
   if (q_seq_stride < 0 || q_head_stride < 0 || block_table_stride < 0) return PA_ERR_INVALID_ARG;
+  if (nr.k && (nr.k_tok_stride < 0 || nr.k_head_stride < 0 || nr.v_tok_stride < 0 ||
+               nr.v_head_stride < 0))
+    return PA_ERR_INVALID_ARG;
   if (!(scale == scale)) return PA_ERR_INVALID_ARG;  // NaN scale
   size_t need = 0;
   int32_t splits = 0;
@@ -156,10 +169,15 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
   if (num_seqs == 0 || max_context_len == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !workspace)
     return PA_ERR_INVALID_ARG;
+  if (nr.k && (!nr.v || !nr.slot_mapping)) return PA_ERR_INVALID_ARG;
   if (workspace_bytes < need) return PA_ERR_WORKSPACE;
   if (splits > 65535 || num_seqs > 65535) return PA_ERR_UNSUPPORTED;  // grid limits
   if (!aligned16(q) || (q_seq_stride * eb) % 16 || (q_head_stride * eb) % 16 ||
       !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+    return PA_ERR_UNSUPPORTED;
+  if (nr.k && (!aligned16(nr.k) || !aligned16(nr.v) || (nr.k_tok_stride * eb) % 16 ||
+               (nr.k_head_stride * eb) % 16 || (nr.v_tok_stride * eb) % 16 ||
+               (nr.v_head_stride * eb) % 16))
     return PA_ERR_UNSUPPORTED;
   float* ws = static_cast<float*>(workspace);
   const size_t acc_elems = static_cast<size_t>(num_seqs) * num_q_heads * splits * head_dim;
@@ -167,8 +185,49 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
                    block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
                    head_dim, block_size, max_context_len, partition_tokens, splits, scale, ws,
                    ws + acc_elems, dtype == PA_DTYPE_BF16,
-                   geom_of(cache_layout, num_kv_heads, block_size, head_dim)};
+                   geom_of(cache_layout, num_kv_heads, block_size, head_dim), nr.k, nr.v,
+                   nr.k_tok_stride, nr.k_head_stride, nr.v_tok_stride, nr.v_head_stride,
+                   nr.slot_mapping};
   return launched(pa::launch_decode(a, stream));
+}
+
+}  // namespace
+
+int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const void* k_cache,
+              const void* v_cache, const int32_t* block_table, int64_t block_table_stride,
+              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+              int32_t cache_layout, int32_t max_context_len, int32_t partition_tokens,
+              float scale, void* workspace, size_t workspace_bytes, int32_t dtype,
+              hipStream_t stream) {
+  return decode_common(q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, cache_layout, max_context_len,
+                       partition_tokens, scale, workspace, workspace_bytes, dtype,
+                       NewRows{nullptr, nullptr, 0, 0, 0, 0, nullptr}, stream);
+}
+
+int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                    int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                    const int32_t* slot_mapping, const void* q, int64_t q_seq_stride,
+                    int64_t q_head_stride, void* k_cache, void* v_cache,
+                    const int32_t* block_table, int64_t block_table_stride,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t cache_layout, int32_t max_context_len,
+                    int32_t partition_tokens, float scale, void* workspace,
+                    size_t workspace_bytes, int32_t dtype, hipStream_t stream) {
+  if (num_seqs > 0 && max_context_len > 0 && (!k_new || !v_new || !slot_mapping))
+    return PA_ERR_INVALID_ARG;
+  if (num_blocks > 0 && block_size > 0 && num_blocks > (INT32_MAX / block_size) + int64_t{1})
+    return PA_ERR_UNSUPPORTED;  // int32 slots
+  return decode_common(q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, cache_layout, max_context_len,
+                       partition_tokens, scale, workspace, workspace_bytes, dtype,
+                       NewRows{k_new, v_new, k_tok_stride, k_head_stride, v_tok_stride,
+                               v_head_stride, slot_mapping},
+                       stream);
 }
 
 int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

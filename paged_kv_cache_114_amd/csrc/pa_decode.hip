@@ -25,6 +25,12 @@
 // * Online softmax in fp32, base-2 (scores pre-multiplied by log2 e and exp2
 //   on the hardware transcendental unit); the split statistics (m, l, acc)
 //   go to the workspace, and the reduce merges them as [Intro §9.5] requires.
+// * Optionally (kStore) the same launch does this step's KV store
+//   [Intro §13.1]: sequence b's new token sits at position context_lens[b]-1,
+//   in the sequence's last split; that split's waves write the token's K and
+//   V rows to slot_mapping[b] and use them from registers in place of the row
+//   they load from the cache, so the store needs no ordering against the
+//   loads and costs no extra launch.
 
 #include <math.h>
 
@@ -46,7 +52,7 @@ struct DecodeShape {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T, int D, int G, int NW>
+template <typename T, int D, int G, int NW, bool kStore>
 __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     const T* __restrict__ q, int64_t q_seq_stride, int64_t q_head_stride,
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
@@ -54,7 +60,9 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_kv_heads,
     int32_t bs_log2, int32_t bt_entries, int32_t partition_tokens, int32_t num_splits,
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t block_stride,
-    int32_t slot_stride, int64_t head_stride) {
+    int32_t slot_stride, int64_t head_stride, const T* k_new, const T* v_new, int64_t k_tok_stride,
+    int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+    const int32_t* slot_mapping, T* k_cache_w, T* v_cache_w) {
   using S = DecodeShape<T, D, G>;
   constexpr int kE = S::kE, kR = S::kR, kTpl = S::kTpl, kU = S::kU, kTile = S::kTile;
   extern __shared__ int32_t bt_lds[];
@@ -89,6 +97,30 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
   const int ctx = context_lens[b];
   if (t0 >= ctx) return;  // empty split (uniform over the workgroup): nothing written
   const int t1 = min(t0 + partition_tokens, ctx);
+  const int bs_mask = (1 << bs_log2) - 1;
+
+  // The fused store.  Only the position ctx - 1 is affected, and only this
+  // split's waves read it: whatever their loads of that row return (old bits
+  // or the new ones) is replaced by these registers where it is used.
+  int new_pos = -1;
+  uint4 k_new_raw = make_uint4(0, 0, 0, 0), v_new_raw = make_uint4(0, 0, 0, 0);
+  if constexpr (kStore) {
+    const int32_t slot = t1 == ctx ? slot_mapping[b] : -1;
+    if (slot >= 0) {
+      new_pos = ctx - 1;
+      k_new_raw = load16(k_new + b * k_tok_stride + g * k_head_stride + col * kE);
+      v_new_raw = load16(v_new + b * v_tok_stride + g * v_head_stride + col * kE);
+      if (row == 0) {
+        const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(slot >> bs_log2)) *
+                                 block_stride +
+                             static_cast<uint32_t>(slot & bs_mask) *
+                                 static_cast<uint32_t>(slot_stride) +
+                             g * head_stride + col * kE;
+        *reinterpret_cast<uint4*>(k_cache_w + off) = k_new_raw;
+        *reinterpret_cast<uint4*>(v_cache_w + off) = v_new_raw;
+      }
+    }
+  }
   __syncthreads();  // bt_lds ready
 
   float qf[G][kE];
@@ -110,7 +142,6 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
 
   const T* kbase = k_cache + g * head_stride + col * kE;
   const T* vbase = v_cache + g * head_stride + col * kE;
-  const int bs_mask = (1 << bs_log2) - 1;
 
   // Loads of tile n+1 are issued before tile n is consumed, so a wave never
   // waits on HBM with nothing else queued.  Rows past t1 read row t1 - 1
@@ -137,7 +168,10 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float kf[kE];
-      Chunk<T>::widen(kr[u], kf);
+      // The fused store's row is taken from registers (a select at use, so the
+      // loads of the next tile stay in flight).
+      const bool is_new = kStore && min(tb + u * kTpl + row, t1 - 1) == new_pos;
+      Chunk<T>::widen(is_new ? k_new_raw : kr[u], kf);
       const bool valid = tb + u * kTpl + row < t1;
 #pragma unroll
       for (int i = 0; i < G; ++i) {
@@ -173,7 +207,8 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float vf[kE];
-      Chunk<T>::widen(vr[u], vf);
+      const bool is_new = kStore && min(tb + u * kTpl + row, t1 - 1) == new_pos;
+      Chunk<T>::widen(is_new ? v_new_raw : vr[u], vf);
 #pragma unroll
       for (int i = 0; i < G; ++i)
 #pragma unroll
@@ -290,38 +325,46 @@ __global__ __launch_bounds__(4 * kWave) void decode_reduce_kernel(
   }
 }
 
-template <typename T, int D, int G, int NW>
+template <typename T, int D, int G, int NW, bool kStore>
 hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
   const int max_blk = (a.partition_tokens >> bs_log2) + 2;
   const int bt_entries = (a.max_context_len + a.block_size - 1) >> bs_log2;
   dim3 grid(a.num_seqs, a.num_kv_heads / NW, a.num_splits);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, NW>), grid, dim3(NW * kWave),
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, NW, kStore>), grid, dim3(NW * kWave),
                      max_blk * sizeof(int32_t), stream, static_cast<const T*>(a.q),
                      a.q_seq_stride, a.q_head_stride, static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_table, a.block_table_stride,
                      a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, bt_entries,
                      a.partition_tokens, a.num_splits, a.scale * kLog2e, a.ws_acc, a.ws_ml,
                      static_cast<uint32_t>(a.geom.block), static_cast<int32_t>(a.geom.slot),
-                     a.geom.head);
+                     a.geom.head, static_cast<const T*>(a.k_new), static_cast<const T*>(a.v_new),
+                     a.k_tok_stride, a.k_head_stride, a.v_tok_stride, a.v_head_stride,
+                     a.slot_mapping, static_cast<T*>(const_cast<void*>(a.k_cache)),
+                     static_cast<T*>(const_cast<void*>(a.v_cache)));
   return hipGetLastError();
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kStore>
 hipError_t pick_nw(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_kv_heads % 8 == 0) return run_partition<T, D, G, 8>(a, stream);
-  if (a.num_kv_heads % 4 == 0) return run_partition<T, D, G, 4>(a, stream);
-  if (a.num_kv_heads % 2 == 0) return run_partition<T, D, G, 2>(a, stream);
-  return run_partition<T, D, G, 1>(a, stream);
+  if (a.num_kv_heads % 8 == 0) return run_partition<T, D, G, 8, kStore>(a, stream);
+  if (a.num_kv_heads % 4 == 0) return run_partition<T, D, G, 4, kStore>(a, stream);
+  if (a.num_kv_heads % 2 == 0) return run_partition<T, D, G, 2, kStore>(a, stream);
+  return run_partition<T, D, G, 1, kStore>(a, stream);
+}
+
+template <typename T, int D, int G>
+hipError_t pick_store(const DecodeArgs& a, hipStream_t stream) {
+  return a.k_new ? pick_nw<T, D, G, true>(a, stream) : pick_nw<T, D, G, false>(a, stream);
 }
 
 template <typename T, int D>
 hipError_t pick_group(const DecodeArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return pick_nw<T, D, 1>(a, stream);
-    case 2: return pick_nw<T, D, 2>(a, stream);
-    case 4: return pick_nw<T, D, 4>(a, stream);
-    case 8: return pick_nw<T, D, 8>(a, stream);
+    case 1: return pick_store<T, D, 1>(a, stream);
+    case 2: return pick_store<T, D, 2>(a, stream);
+    case 4: return pick_store<T, D, 4>(a, stream);
+    case 8: return pick_store<T, D, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

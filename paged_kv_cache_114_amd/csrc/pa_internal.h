@@ -46,6 +46,11 @@ struct DecodeArgs {
   float* ws_ml;   // [B, Hq, S, 2]
   bool bf16;
   CacheGeom geom;
+  // the fused store (k_new == nullptr: none): row b is sequence b's new token
+  const void* k_new;
+  const void* v_new;
+  int64_t k_tok_stride, k_head_stride, v_tok_stride, v_head_stride;
+  const int32_t* slot_mapping;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
