@@ -510,10 +510,11 @@ def cpu_baseline(name, budget_s=12.0, all_cores_s=8.0):
 def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch=None,
                  fused=False):
     """A decode step of a layers-deep model at one workload's shapes: per layer,
-    store + partition + reduce on that layer's own cache, all on one stream.
-    Timed eager (3 launches per layer) and as one captured HIP graph replay.
-    ``fused``: the store is the q/k norm + rope + store step on the layer's
-    projection rows, and the decode reads the rotated Q it writes."""
+    the store fused into the partition pass, then the reduce, on that layer's
+    own cache, all on one stream.  Timed eager and as one captured HIP graph
+    replay.  ``fused``: the store is the q/k norm + rope + store step on the
+    layer's projection rows, then the partition pass reads the rotated Q it
+    writes (3 launches per layer)."""
     import torch
 
     import paged_kv_cache_114_amd as pa
@@ -539,12 +540,12 @@ def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch
                                          proj["k_norm_weight"], proj["positions"],
                                          proj["slot_mapping"], hq, hkv, 1e-6, 1e6, lay["q_rot"],
                                          lay["k_cache"], lay["v_cache"])
+                pa.pa_decode(lay["q_rot"], lay["k_cache"], lay["v_cache"], lay["block_table"],
+                             lay["context_lens"], case.max_context_len, p, case.scale, ws)
             else:
-                pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
-                               lay["slot_mapping"])
-            pa.pa_decode(lay["q_rot"] if fused else lay["q"], lay["k_cache"], lay["v_cache"],
-                         lay["block_table"],
-                         lay["context_lens"], case.max_context_len, p, case.scale, ws)
+                pa.pa_store_decode(lay["k_new"], lay["v_new"], lay["slot_mapping"], lay["q"],
+                                   lay["k_cache"], lay["v_cache"], lay["block_table"],
+                                   lay["context_lens"], case.max_context_len, p, case.scale, ws)
             pa.pa_decode_reduce(ws, lay["context_lens"], splits, p, lay["out"])
 
     flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
@@ -573,9 +574,10 @@ def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch
     torch.cuda.synchronize()
     graph_ms = timed(graph.replay)
     kv = layers * case.kv_bytes_logical()
-    first = "q/k norm + rope + store" if fused else "store"
-    return {"workload": f"{case.name} x {layers} layers ({first} + decode + reduce per layer)",
-            "layers": layers, "launches_per_step": 3 * layers,
+    per_layer = ("q/k norm + rope + store, decode, reduce" if fused
+                 else "store fused into decode, reduce")
+    return {"workload": f"{case.name} x {layers} layers ({per_layer} per layer)",
+            "layers": layers, "launches_per_step": (3 if fused else 2) * layers,
             "eager_ms_per_step": round(eager_ms, 4), "graph_ms_per_step": round(graph_ms, 4),
             "graph_speedup": round(eager_ms / graph_ms, 3),
             "kv_GBps_graph": round(kv / (graph_ms * 1e-3) / 1e9, 1),

@@ -39,27 +39,35 @@ def make_layers(case, n, seed):
     return layers
 
 
-def decode_step(case, layers, ws, splits, partition):
+def decode_step(case, layers, ws, splits, partition, fused=False):
     for lay in layers:
-        pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
-                       lay["slot_mapping"])
-        pa.pa_decode(lay["q"], lay["k_cache"], lay["v_cache"], lay["block_table"],
-                     lay["context_lens"], case.max_context_len, partition, case.scale, ws)
+        if fused:
+            pa.pa_store_decode(lay["k_new"], lay["v_new"], lay["slot_mapping"], lay["q"],
+                               lay["k_cache"], lay["v_cache"], lay["block_table"],
+                               lay["context_lens"], case.max_context_len, partition, case.scale,
+                               ws)
+        else:
+            pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
+                           lay["slot_mapping"])
+            pa.pa_decode(lay["q"], lay["k_cache"], lay["v_cache"], lay["block_table"],
+                         lay["context_lens"], case.max_context_len, partition, case.scale, ws)
         pa.pa_decode_reduce(ws, lay["context_lens"], splits, partition, lay["out"])
 
 
-@pytest.mark.parametrize("lengths,pad", [
-    ([1000, 17, 300, 513, 256, 1, 64, 700, 129, 900, 2], 5),   # 11 sequences in bucket 16
-    ([40], 0),                                                  # bucket 1
+@pytest.mark.parametrize("lengths,pad,fused", [
+    ([1000, 17, 300, 513, 256, 1, 64, 700, 129, 900, 2], 5, False),  # 11 sequences, bucket 16
+    ([40], 0, False),                                                 # bucket 1
+    ([1000, 17, 300, 513, 256, 1, 64, 700, 129, 900, 2], 5, True),   # store fused into decode
 ])
-def test_graph_decode_step_replays_equal_eager(lengths, pad):
+def test_graph_decode_step_replays_equal_eager(lengths, pad, fused):
     case = W.decode_case(f"graph_{len(lengths)}", 91, lengths=lengths, pad_rows=pad)
-    print(f"graph case={case.name} B={case.num_seqs} layers={LAYERS}", flush=True)
+    print(f"graph case={case.name} B={case.num_seqs} layers={LAYERS} fused={fused}", flush=True)
     partition = 256
     layers = make_layers(case, LAYERS, seed=7)
     ws, _, splits = decode_buffers(case, partition)
+    step = lambda: decode_step(case, layers, ws, splits, partition, fused)  # noqa: E731
 
-    decode_step(case, layers, ws, splits, partition)
+    step()
     torch.cuda.synchronize()
     eager = [lay["out"].clone() for lay in layers]
 
@@ -67,11 +75,11 @@ def test_graph_decode_step_replays_equal_eager(lengths, pad):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        decode_step(case, layers, ws, splits, partition)   # warm-up on the capture stream
+        step()   # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        decode_step(case, layers, ws, splits, partition)
+        step()
     torch.cuda.synchronize()
 
     bits = torch.int16
@@ -89,7 +97,7 @@ def test_graph_decode_step_replays_equal_eager(lengths, pad):
     gen.manual_seed(8)
     for lay in layers:
         lay["q"].copy_(torch.randn(lay["q"].shape, generator=gen, device=DEV))
-    decode_step(case, layers, ws, splits, partition)
+    step()
     torch.cuda.synchronize()
     eager2 = [lay["out"].clone() for lay in layers]
     for lay in layers:
