@@ -94,33 +94,25 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
   for (int i = 0; i < G; ++i)
     q_raw[i] = load16(q + static_cast<int64_t>(b) * q_seq_stride +
                       static_cast<int64_t>(g * G + i) * q_head_stride + col * kE);
+  // The fused store's inputs are loaded with the rest, whether or not this is
+  // the sequence's last split, so no dependent load sits before the tiles.
+  int32_t slot = -1;
+  uint4 k_new_raw = make_uint4(0, 0, 0, 0), v_new_raw = make_uint4(0, 0, 0, 0);
+  if constexpr (kStore) {
+    slot = slot_mapping[b];
+    k_new_raw = load16(k_new + b * k_tok_stride + g * k_head_stride + col * kE);
+    v_new_raw = load16(v_new + b * v_tok_stride + g * v_head_stride + col * kE);
+  }
   const int ctx = context_lens[b];
   if (t0 >= ctx) return;  // empty split (uniform over the workgroup): nothing written
   const int t1 = min(t0 + partition_tokens, ctx);
   const int bs_mask = (1 << bs_log2) - 1;
 
-  // The fused store.  Only the position ctx - 1 is affected, and only this
-  // split's waves read it: whatever their loads of that row return (old bits
-  // or the new ones) is replaced by these registers where it is used.
-  int new_pos = -1;
-  uint4 k_new_raw = make_uint4(0, 0, 0, 0), v_new_raw = make_uint4(0, 0, 0, 0);
-  if constexpr (kStore) {
-    const int32_t slot = t1 == ctx ? slot_mapping[b] : -1;
-    if (slot >= 0) {
-      new_pos = ctx - 1;
-      k_new_raw = load16(k_new + b * k_tok_stride + g * k_head_stride + col * kE);
-      v_new_raw = load16(v_new + b * v_tok_stride + g * v_head_stride + col * kE);
-      if (row == 0) {
-        const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(slot >> bs_log2)) *
-                                 block_stride +
-                             static_cast<uint32_t>(slot & bs_mask) *
-                                 static_cast<uint32_t>(slot_stride) +
-                             g * head_stride + col * kE;
-        *reinterpret_cast<uint4*>(k_cache_w + off) = k_new_raw;
-        *reinterpret_cast<uint4*>(v_cache_w + off) = v_new_raw;
-      }
-    }
-  }
+  // The fused store: only position ctx - 1 of the last split is affected, and
+  // only this split's waves read it; its rows are used from registers where
+  // the tile loads would supply them (whatever those loads return is
+  // discarded), and written to the cache at the end.
+  const int new_pos = kStore && t1 == ctx && slot >= 0 ? ctx - 1 : -1;
   __syncthreads();  // bt_lds ready
 
   float qf[G][kE];
@@ -249,6 +241,16 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
       for (int e = 0; e < kE; e += 4)
         dst[e / 4] = make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
       if (col == 0) reinterpret_cast<float2*>(ws_ml)[idx] = make_float2(m[i], l[i]);
+    }
+  }
+  if constexpr (kStore) {
+    if (new_pos >= 0 && row == 0) {
+      const uint64_t off =
+          static_cast<uint64_t>(static_cast<uint32_t>(slot >> bs_log2)) * block_stride +
+          static_cast<uint32_t>(slot & bs_mask) * static_cast<uint32_t>(slot_stride) +
+          g * head_stride + col * kE;
+      *reinterpret_cast<uint4*>(k_cache_w + off) = k_new_raw;
+      *reinterpret_cast<uint4*>(v_cache_w + off) = v_new_raw;
     }
   }
 }
