@@ -4,8 +4,9 @@
 A step is one pass of the hot path over one batch of synthetic input: for a
 decode workload, pa_store_decode (this step's K/V rows stored, and the split-K
 partition pass, in one launch) -> pa_decode_reduce; for the prefill workload,
-pa_store_kv -> pa_prefill_varlen.  The two-call decode step (pa_store_kv ->
-pa_decode -> pa_decode_reduce) is reported beside it.  Inputs are resident in HBM before timing starts.  Before
+pa_store_prefill_varlen (the store in the work-list launch, then the tile
+kernel).  The two-call steps (pa_store_kv, then pa_decode -> pa_decode_reduce
+or pa_prefill_varlen) are reported beside them.  Inputs are resident in HBM before timing starts.  Before
 every step a 1 GiB buffer is read (outside the timed events) so the 256 MB
 Infinity Cache and the L2s hold no KV: a real engine touches 28 layers'
 caches between two visits to one layer.  The flush only reads, so it leaves
@@ -190,12 +191,12 @@ class Runner:
         pa, v, c = self.pa, self.vals, self.case
         mark = ev.record if inner else (lambda i: None)
         ev.record(4 * k)
-        fused = self.kind == "decode" and self.fused_store
+        fused = self.fused_store
         if not fused:
             pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"], v["slot_mapping"],
                            layout=self.layout)
         mark(4 * k + 1)
-        if fused:  # the store and the partition pass in one launch
+        if fused and self.kind == "decode":  # the store and the partition pass in one launch
             pa.pa_store_decode(v["k_new"], v["v_new"], v["slot_mapping"], v["q"], v["k_cache"],
                                v["v_cache"], v["block_table"], v["context_lens"],
                                c.max_context_len, self.partition, c.scale, self.ws,
@@ -209,6 +210,13 @@ class Runner:
             mark(4 * k + 2)
             pa.pa_decode_reduce(self.ws, v["context_lens"], self.splits, self.partition,
                                 self.out)
+        elif self.fused_store:  # the store runs in the prefill's work-list launch
+            pa.pa_store_prefill_varlen(v["k_new"], v["v_new"], v["slot_mapping"], v["q"],
+                                       v["k_cache"], v["v_cache"], v["cu_seqlens_q"],
+                                       v["cu_seqlens_k"], v["block_table"], c.max_seqlen_q,
+                                       c.max_context_len, c.scale, self.out, self.ws,
+                                       split_keys=self.split_keys, layout=self.layout)
+            mark(4 * k + 2)
         else:
             pa.pa_prefill_varlen(v["q"], v["k_cache"], v["v_cache"], v["cu_seqlens_q"],
                                  v["cu_seqlens_k"], v["block_table"], c.max_seqlen_q,
@@ -313,7 +321,8 @@ class Runner:
             return out
         flops = self.prefill_flops()
         tf = flops / (t["main_ms"] * 1e-3) / 1e12
-        return {"workload": c.name, "layout": self.layout, "prefill_TFLOPs_kernel": round(tf, 2),
+        return {"workload": c.name, "layout": self.layout, "fused_store": self.fused_store,
+                "prefill_TFLOPs_kernel": round(tf, 2),
                 "frac_bf16_mfma": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                 "ms_per_step": round(t["step_ms"], 5), "prefill_kernel_ms": round(t["main_ms"], 5),
                 "gflop": round(flops / 1e9, 3), "split_keys": self.split_keys,
@@ -720,6 +729,7 @@ def main():
         import workloads as W
         variants = [("c2_two_call", "c2", "bshd", None, False),
                     ("c4_two_call", "c4", "bshd", None, False),
+                    ("c3_two_call", "c3", "bshd", None, False),
                     ("layout_bhsd_c2", "c2", "bhsd", None, True),
                     ("layout_bhsd_c3", "c3", "bhsd", None, True)]
         for bs in (16, 64):

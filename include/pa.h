@@ -325,6 +325,38 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
                       int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
                       hipStream_t stream);
 
+/*
+ * pa_store_prefill_varlen -- pa_store_kv of this step's new rows and
+ * pa_prefill_varlen, with the store done in the same launch as the work-list
+ * build.
+ *
+ * [Intro §13.1, §13.2]: the prefill step stores the new tokens' K/V, then
+ * attends over the paged cache.  The new tokens are the query rows: row i of
+ * k_new / v_new is query row i's token and goes to slot slot_mapping[i] (-1:
+ * not stored), exactly as pa_store_kv writes it.  The output and the pool are
+ * bit for bit those of pa_store_kv followed by pa_prefill_varlen.
+ *
+ *   k_new, v_new   [total_q, num_kv_heads, head_dim] of dtype, strides
+ *                  k_tok_stride / k_head_stride and v_tok_stride /
+ *                  v_head_stride (elements, 16-byte aligned rows).
+ *   slot_mapping   int32 [total_q].
+ * Every other argument is as for pa_prefill_varlen; the caches are written,
+ * so they are not const here.
+ */
+int pa_store_prefill_varlen(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                            int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                            const int32_t* slot_mapping, const void* q, int64_t q_tok_stride,
+                            int64_t q_head_stride, void* k_cache, void* v_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int32_t cache_layout, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, float scale, int32_t split_keys,
+                            void* workspace, size_t workspace_bytes, void* out,
+                            int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,7 @@ EXPORTS = (
     "pa_decode_reduce",
     "pa_prefill_workspace_size",
     "pa_prefill_varlen",
+    "pa_store_prefill_varlen",
 )
 
 
@@ -84,6 +85,11 @@ def _load():
     lib.pa_prefill_varlen.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                       i32, i32, i64, i32, i32, i32, f32, i32, vp, sz, vp, i64,
                                       i64, i32, vp]
+    lib.pa_store_prefill_varlen.restype = ctypes.c_int
+    lib.pa_store_prefill_varlen.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp,
+                                            vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i64,
+                                            i32, i32, i32, f32, i32, vp, sz, vp, i64, i64, i32,
+                                            vp]
     return lib
 
 
@@ -243,3 +249,21 @@ def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tab
         tq, hq, hkv, d, bs, nb, lay, max_seqlen_q, max_seqlen_k, scale, split_keys,
         _ptr(workspace), ws_bytes, _ptr(out), out.stride(0), out.stride(1), _dtype_code(q),
         _stream(stream)))
+
+
+def pa_store_prefill_varlen(k_new, v_new, slot_mapping, q, k_cache, v_cache, cu_seqlens_q,
+                            cu_seqlens_k, block_table, max_seqlen_q, max_seqlen_k, scale, out,
+                            workspace, split_keys=0, stream=None, layout="bshd") -> None:
+    """Store the query rows' K/V (``[Tq, Hkv, d]``) through ``slot_mapping`` and run the
+    causal varlen prefill, the store in the same launch as the work-list build."""
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    tq, hq, _ = q.shape
+    assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("pa_store_prefill_varlen", library().pa_store_prefill_varlen(
+        _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1), v_new.stride(0),
+        v_new.stride(1), _ptr(slot_mapping), _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache),
+        _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(block_table),
+        block_table.stride(0), cu_seqlens_q.shape[0] - 1, tq, hq, hkv, d, bs, nb, lay,
+        max_seqlen_q, max_seqlen_k, scale, split_keys, _ptr(workspace), ws_bytes, _ptr(out),
+        out.stride(0), out.stride(1), _dtype_code(q), _stream(stream)))

@@ -128,7 +128,7 @@ int pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head
 
 namespace {
 
-struct NewRows {  // the fused store of pa_store_decode (k == nullptr: none)
+struct NewRows {  // the fused store of pa_store_decode / pa_store_prefill_varlen (k null: none)
   const void* k;
   const void* v;
   int64_t k_tok_stride, k_head_stride, v_tok_stride, v_head_stride;
@@ -304,16 +304,18 @@ int pa_prefill_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_h
   return PA_OK;
 }
 
-int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
-                      const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
-                      const int32_t* cu_seqlens_k, const int32_t* block_table,
-                      int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
-                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t block_size, int64_t num_blocks, int32_t cache_layout,
-                      int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
-                      int32_t split_keys, void* workspace, size_t workspace_bytes, void* out,
-                      int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
-                      hipStream_t stream) {
+namespace {
+
+int prefill_common(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                   const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+                   const int32_t* cu_seqlens_k, const int32_t* block_table,
+                   int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                   int32_t max_seqlen_q, int32_t max_seqlen_k, float scale, int32_t split_keys,
+                   void* workspace, size_t workspace_bytes, void* out, int64_t out_tok_stride,
+                   int64_t out_head_stride, int32_t dtype, const NewRows& nr,
+                   hipStream_t stream) {
   const int eb = elt_bytes(dtype);
   if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_blocks <= 0 ||
@@ -329,6 +331,9 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
   if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
   if (q_tok_stride < 0 || q_head_stride < 0 || out_tok_stride < 0 || out_head_stride < 0 ||
       block_table_stride < 0)
+    return PA_ERR_INVALID_ARG;
+  if (nr.k && (nr.k_tok_stride < 0 || nr.k_head_stride < 0 || nr.v_tok_stride < 0 ||
+               nr.v_head_stride < 0))
     return PA_ERR_INVALID_ARG;
   if (!(scale > 0.f)) return PA_ERR_INVALID_ARG;  // also rejects NaN
   size_t need = 0;
@@ -349,14 +354,25 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_table || !out ||
       !workspace)
     return PA_ERR_INVALID_ARG;
+  if (nr.k && (!nr.v || !nr.slot_mapping)) return PA_ERR_INVALID_ARG;
   if (workspace_bytes < need) return PA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (q_tok_stride * eb) % 16 || (q_head_stride * eb) % 16 || (out_tok_stride * eb) % 16 ||
       (out_head_stride * eb) % 16)
     return PA_ERR_UNSUPPORTED;
+  if (nr.k && (!aligned16(nr.k) || !aligned16(nr.v) || (nr.k_tok_stride * eb) % 16 ||
+               (nr.k_head_stride * eb) % 16 || (nr.v_tok_stride * eb) % 16 ||
+               (nr.v_head_stride * eb) % 16))
+    return PA_ERR_UNSUPPORTED;
   const PrefillLayout lay =
       prefill_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, splits);
+  const pa::CacheGeom geom = geom_of(cache_layout, num_kv_heads, block_size, head_dim);
+  // the store of this step's rows (one per query row), when asked for
+  const pa::StoreArgs store{nr.k, nr.v, nr.k_tok_stride, nr.k_head_stride, nr.v_tok_stride,
+                            nr.v_head_stride, const_cast<void*>(k_cache),
+                            const_cast<void*>(v_cache), nr.slot_mapping, total_q, num_kv_heads,
+                            head_dim, block_size, eb, geom};
   pa::PrefillArgs a{q, q_tok_stride, q_head_stride, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
                     block_table, block_table_stride, num_seqs, num_q_heads, num_kv_heads,
                     head_dim, block_size, max_seqlen_q, max_seqlen_k, total_q, scale,
@@ -365,9 +381,53 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
                     reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.merges_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off),
-                    out, out_tok_stride, out_head_stride,
-                    geom_of(cache_layout, num_kv_heads, block_size, head_dim)};
+                    out, out_tok_stride, out_head_stride, geom, nr.k ? &store : nullptr};
   return launched(pa::launch_prefill(a, stream));
+}
+
+}  // namespace
+
+int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                      const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, const int32_t* block_table,
+                      int64_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, int32_t cache_layout,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                      int32_t split_keys, void* workspace, size_t workspace_bytes, void* out,
+                      int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
+                      hipStream_t stream) {
+  return prefill_common(q, q_tok_stride, q_head_stride, k_cache, v_cache, cu_seqlens_q,
+                        cu_seqlens_k, block_table, block_table_stride, num_seqs, total_q,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        cache_layout, max_seqlen_q, max_seqlen_k, scale, split_keys, workspace,
+                        workspace_bytes, out, out_tok_stride, out_head_stride, dtype,
+                        NewRows{nullptr, nullptr, 0, 0, 0, 0, nullptr}, stream);
+}
+
+int pa_store_prefill_varlen(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                            int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                            const int32_t* slot_mapping, const void* q, int64_t q_tok_stride,
+                            int64_t q_head_stride, void* k_cache, void* v_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int32_t cache_layout, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, float scale, int32_t split_keys,
+                            void* workspace, size_t workspace_bytes, void* out,
+                            int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
+                            hipStream_t stream) {
+  if (num_seqs > 0 && total_q > 0 && max_seqlen_q > 0 && (!k_new || !v_new || !slot_mapping))
+    return PA_ERR_INVALID_ARG;
+  return prefill_common(q, q_tok_stride, q_head_stride, k_cache, v_cache, cu_seqlens_q,
+                        cu_seqlens_k, block_table, block_table_stride, num_seqs, total_q,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        cache_layout, max_seqlen_q, max_seqlen_k, scale, split_keys, workspace,
+                        workspace_bytes, out, out_tok_stride, out_head_stride, dtype,
+                        NewRows{k_new, v_new, k_tok_stride, k_head_stride, v_tok_stride,
+                                v_head_stride, slot_mapping},
+                        stream);
 }
 
 }  // extern "C"

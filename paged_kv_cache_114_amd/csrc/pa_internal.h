@@ -30,6 +30,10 @@ struct StoreArgs {
   CacheGeom geom;
 };
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
+struct StoreRows;
+// The row-copy description of a store (false: a shape the copy cannot take).
+template <typename W>
+bool store_rows_args(const StoreArgs& a, StoreRows* r);
 
 struct DecodeArgs {
   const void* q;
@@ -86,6 +90,7 @@ struct PrefillArgs {
   void* out;
   int64_t out_tok_stride, out_head_stride;
   CacheGeom geom;
+  const StoreArgs* store;  // non-null: this step's K/V store, in the work-list launch
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -50,6 +50,7 @@
 
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_store_rows.h"
 
 namespace pa {
 namespace {
@@ -537,7 +538,7 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 1024;  // weights >= kPlanBins - 1 share the last bin
 
 template <int BM>
-__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+__device__ __forceinline__ void plan_body(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
     int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
     int2* __restrict__ items, int2* __restrict__ merges) {
@@ -654,6 +655,33 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   }
 }
 
+template <int BM>
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
+    int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
+    int2* __restrict__ items, int2* __restrict__ merges) {
+  plan_body<BM>(cu_q, cu_k, num_seqs, split_tiles, num_kv_heads, tickets, items, merges);
+}
+
+// The work list and this step's KV store in one launch: workgroup 0 builds
+// the list while the others copy the new rows into the cache.  Both must be
+// done before the tile kernel starts, which stream order gives; one launch
+// instead of two removes a launch and lets the list build overlap the copy.
+template <int BM>
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_store_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
+    int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
+    int2* __restrict__ items, int2* __restrict__ merges, StoreRows store) {
+  if (blockIdx.x == 0) {
+    plan_body<BM>(cu_q, cu_k, num_seqs, split_tiles, num_kv_heads, tickets, items, merges);
+    return;
+  }
+  constexpr int kWaves = kPlanThreads / kWave;
+  store_rows<uint4>(store,
+                    (blockIdx.x - 1) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave),
+                    (gridDim.x - 1) * kWaves);
+}
+
 // Merge of the key-range partials of split query tiles ([Intro §9.5]: each
 // partial carries its own maximum m_s and sum l_s, so the output is
 // sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s with m* = max_s m_s).
@@ -736,9 +764,21 @@ hipError_t run(const PrefillArgs& a, hipStream_t stream) {
   const size_t bt_bytes = static_cast<size_t>((a.max_seqlen_k + a.block_size - 1) >> bs_log2) * 4;
   // split_tiles >= every tile's key-tile count when nothing is split
   const int split_tiles = a.num_splits > 1 ? a.split_keys / kBN : (a.max_seqlen_k + kBN - 1) / kBN;
-  hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
-                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, split_tiles, a.num_kv_heads,
-                     a.tickets, a.items, a.merges);
+  if (a.store) {
+    StoreRows rows;
+    if (!store_rows_args<uint4>(*a.store, &rows)) return hipErrorInvalidValue;
+    constexpr int kWaves = kPlanThreads / kWave;
+    const int64_t want = (int64_t{rows.rows} + kWaves - 1) / kWaves;
+    const int store_blocks = static_cast<int>(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL((prefill_plan_store_kernel<S::kBM>), dim3(1 + store_blocks),
+                       dim3(kPlanThreads), 0, stream, a.cu_seqlens_q, a.cu_seqlens_k,
+                       a.num_seqs, split_tiles, a.num_kv_heads, a.tickets, a.items, a.merges,
+                       rows);
+  } else {
+    hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
+                       a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, split_tiles, a.num_kv_heads,
+                       a.tickets, a.items, a.merges);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // one workgroup per resident slot: they stay until the work list is empty

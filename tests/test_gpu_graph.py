@@ -120,7 +120,8 @@ def test_graph_decode_step_replays_equal_eager(lengths, pad, fused):
         assert_close(got[:real], host.decode(), case.dtype, f"layer {i}")
 
 
-def test_graph_prefill_step_replays_equal_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_prefill_step_replays_equal_eager(fused):
     """Four layers of a varlen prefill (store, then the work-list plan, the
     persistent tile kernel and, with key-range splits, the merge): the plan kernel
     resets its own counter on the device, so every replay redoes the whole
@@ -136,6 +137,13 @@ def test_graph_prefill_step_replays_equal_eager():
 
         def step():
             for lay in layers:
+                if fused:  # the store in the work-list launch
+                    pa.pa_store_prefill_varlen(
+                        lay["k_new"], lay["v_new"], lay["slot_mapping"], lay["q"],
+                        lay["k_cache"], lay["v_cache"], lay["cu_seqlens_q"], lay["cu_seqlens_k"],
+                        lay["block_table"], case.max_seqlen_q, case.max_context_len, case.scale,
+                        lay["out"], ws, split_keys=split_keys)
+                    continue
                 pa.pa_store_kv(lay["k_new"], lay["v_new"], lay["k_cache"], lay["v_cache"],
                                lay["slot_mapping"])
                 pa.pa_prefill_varlen(lay["q"], lay["k_cache"], lay["v_cache"],

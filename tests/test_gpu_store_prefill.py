@@ -1,0 +1,75 @@
+"""pa_store_prefill_varlen (this step's rows stored in the work-list launch) against the
+two-call path pa_store_kv + pa_prefill_varlen, bit for bit, and against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from pa_runner import DEV, HostInputs, assert_close, prefill_workspace, to_f64
+
+import paged_kv_cache_114_amd as pa
+
+pytestmark = pytest.mark.gpu
+
+
+def swap_slots_heads(cache):
+    return cache.permute(0, 2, 1, 3).contiguous()
+
+
+def run(case, vals, fused, layout, split_keys):
+    kc, vc = vals["k_cache"].clone(), vals["v_cache"].clone()
+    if layout == "bhsd":
+        kc, vc = swap_slots_heads(kc), swap_slots_heads(vc)
+    out = torch.full_like(vals["q"], float("nan"))
+    ws = prefill_workspace(case, split_keys)
+    args = (vals["cu_seqlens_q"], vals["cu_seqlens_k"], vals["block_table"], case.max_seqlen_q,
+            case.max_context_len, case.scale, out, ws)
+    if fused:
+        pa.pa_store_prefill_varlen(vals["k_new"], vals["v_new"], vals["slot_mapping"], vals["q"],
+                                   kc, vc, *args, split_keys=split_keys, layout=layout)
+    else:
+        pa.pa_store_kv(vals["k_new"], vals["v_new"], kc, vc, vals["slot_mapping"], layout=layout)
+        pa.pa_prefill_varlen(vals["q"], kc, vc, *args, split_keys=split_keys, layout=layout)
+    torch.cuda.synchronize()
+    if layout == "bhsd":
+        kc, vc = swap_slots_heads(kc), swap_slots_heads(vc)
+    return out, kc, vc
+
+
+def check(case, layout="bshd", split_keys=0, oracle_seqs=None):
+    print(f"store_prefill case={case.name} T={case.num_new_tokens} layout={layout} "
+          f"split_keys={split_keys}", flush=True)
+    vals = W.materialize(case, DEV)
+    k_before = W.raw_numpy(vals["k_cache"], case.dtype)
+    v_before = W.raw_numpy(vals["v_cache"], case.dtype)
+    host = HostInputs(case, vals, oracle_seqs)
+    out_f, kc_f, vc_f = run(case, vals, True, layout, split_keys)
+    out_s, _, _ = run(case, vals, False, layout, split_keys)
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), "fused != two-call"
+    k_want, v_want = oracle.store(k_before, v_before, W.raw_numpy(vals["k_new"], case.dtype),
+                                  W.raw_numpy(vals["v_new"], case.dtype), case.slot_mapping)
+    assert np.array_equal(W.raw_numpy(kc_f, case.dtype), k_want), "K pool"
+    assert np.array_equal(W.raw_numpy(vc_f, case.dtype), v_want), "V pool"
+    assert_close(to_f64(out_f, case.dtype)[host.token_rows], host.prefill(), case.dtype,
+                 case.name)
+
+
+@pytest.mark.parametrize("name", ["c3s", "mixeds"])
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+def test_store_prefill_small(name, layout):
+    check(W.SMALL_CASES[name](), layout)
+
+
+def test_store_prefill_small_blocks_and_splits():
+    case = W.prefill_case("sp_bs16", 5300, lengths=[700, 1500, 33, 260], cached=[0, 17, 0, 256],
+                          bs=16)
+    check(case)
+    check(case, split_keys=256)
+
+
+@pytest.mark.parametrize("name", ["c3", "mixed"])
+def test_store_prefill_full(name):
+    case = W.FULL_CASES[name]()
+    check(case, oracle_seqs=[0, case.num_seqs // 2, case.num_seqs - 1])
