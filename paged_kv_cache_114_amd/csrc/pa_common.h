@@ -83,6 +83,14 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// The value of lane i ^ 32: one v_permlane32_swap (the two halves of a copy
+// traded) and a select, instead of a round trip through the LDS unit.
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+}
+
 // Max across lanes that differ only in the lane bits from kFrom up to the wave.
 template <int kFrom>
 __device__ __forceinline__ float across_groups_max(float x) {

@@ -320,17 +320,29 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   float m_ref = -INFINITY;
   float l_run = 0.f;  // this lane's share of the exponential sum
 
-  // S^T = K Q^T for one 64-key tile: two 32-key accumulator chains.
+  // S^T = K Q^T for one 64-key tile: two 32-key accumulator chains.  The K
+  // operand reads run kLead steps ahead of their MFMAs, in an order the
+  // scheduler may not change: left to itself it issued each read right before
+  // its MFMA, which then waited the LDS latency (C3 62.2 -> 58.2 us, mixed
+  // batch 66.6 -> 61.5 us; leads of 3 and 4 were no better).
   auto qk = [&](const uint16_t* kt_lds, f32x16_t (&acc_s)[2]) {
     acc_s[0] = f32x16_t{};
     acc_s[1] = f32x16_t{};
-#pragma unroll
-    for (int s = 0; s < S::kSteps; ++s) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(kt_lds + k_off[s]);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(kt_lds + k_off[s] + 32 * D);
-      acc_s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[s], acc_s[0], 0, 0, 0);
-      acc_s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), qf[s], acc_s[1], 0, 0, 0);
-    }
+    constexpr int kLead = 2;
+    uint4 a0[S::kSteps], a1[S::kSteps];
+    static_for<0, S::kSteps + kLead>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < S::kSteps) {
+        a0[i] = *reinterpret_cast<const uint4*>(kt_lds + k_off[i]);
+        a1[i] = *reinterpret_cast<const uint4*>(kt_lds + k_off[i] + 32 * D);
+      }
+      if constexpr (i >= kLead) {
+        constexpr int s = i - kLead;
+        acc_s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0[s]), qf[s], acc_s[0], 0, 0, 0);
+        acc_s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1[s]), qf[s], acc_s[1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // One tile: S^T = K Q^T, the causal mask where the tile reaches past the
@@ -355,7 +367,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc_s[mb][r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;  // scale_log2 > 0
+    tmax = fmaxf(tmax, lane_xor32(tmax)) * scale_log2;  // scale_log2 > 0
     if (__ballot(tmax > m_ref + kLazy)) {  // wave-uniform: raise the reference
       const float m_new = fmaxf(m_ref, tmax);
       // a row that has seen no key yet (m_ref = m_new = -inf) keeps alpha = 1
@@ -493,7 +505,7 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   else
     key_loop(std::false_type{});
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = l_run + lane_xor32(l_run);
   if (row_ok && n_split > 1) {
     // Partial result of this key range, against its own reference maximum:
     // acc [split][row][head][D] un-normalised, ml [split][row][head] = (m, l).
