@@ -234,7 +234,10 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   const int my_row = w_q0 + col;                            // this lane's query row
   const bool row_ok = my_row < lq;
   const int my_pos = ctx0 + my_row;                         // its position in the sequence
-  const int w_last_pos = ctx0 + min(lq - 1, w_q0 + 31);     // last position the wave needs
+  // last position the wave needs; -1 for a wave whose rows all lie past the
+  // sequence (a ragged last tile, a decode row's empty row block): it only
+  // moves tiles and meets the barriers (mixed batch 63.5 -> 61.1 us)
+  const int w_last_pos = w_q0 < lq ? ctx0 + min(lq - 1, w_q0 + 31) : -1;
   // A row that sees fewer than kRestKeys keys can put most of its weight on a
   // few of them, where rounding p to bf16 (relative error up to 2^-9) can move
   // the output by more than the 2e-3 absolute bound when the weighted values
