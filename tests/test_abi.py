@@ -236,3 +236,24 @@ def test_norm_rope_store_validation():
     assert rope(qw=odd, kw=fake, **ptrs) == pa.PA_ERR_UNSUPPORTED  # misaligned weights
     # group sizes the attention kernels reject are fine here
     assert rope(hq=12, hkv=2, qs=16 * 128, qos=12 * 128, t=0) == pa.PA_OK
+
+
+def test_header_is_c_and_a_c_program_links_the_library(tmp_path):
+    """include/pa.h compiles as C11 and a C program linked against libpa.so gets the
+    documented host-side answers (tests/c/abi_check.c; no kernel is launched)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "c", "abi_check.c")
+    exe = str(tmp_path / "abi_check")
+    libdir = os.path.dirname(pa.LIB_PATH)
+    cmd = [gcc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src, "-o", exe,
+           "-L", libdir, "-l:libpa.so", f"-Wl,-rpath,{libdir}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "all checks passed" in run.stdout
