@@ -84,3 +84,20 @@ def test_store_decode_padding_rows():
 
 def test_store_decode_full_c2():
     check(W.FULL_CASES["c2"]())
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype,bs", [
+    (8, 8, 128, "bf16", 256),    # group 1
+    (16, 4, 128, "bf16", 64),    # group 4
+    (16, 2, 128, "bf16", 16),    # group 8
+    (16, 8, 64, "bf16", 32),     # head_dim 64
+    (4, 2, 128, "f32", 16),      # fp32, head_dim 128
+    (24, 3, 128, "bf16", 8),     # odd kv-head count, smallest block
+])
+def test_store_decode_shapes(hq, hkv, d, dtype, bs):
+    """Every GQA group, head_dim and element type the fused launch is built for."""
+    case = W.decode_case(f"sdshape_{hq}_{hkv}_{d}_{dtype}_{bs}", 5400 + hq + bs,
+                         lengths=[1, 63, 64, 65, 129, 512, 513, 1000], hq=hq, hkv=hkv, d=d,
+                         dtype=dtype, bs=bs)
+    check(case, partition=64)
+    check(case, partition=256, layout="bhsd")

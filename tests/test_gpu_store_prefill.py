@@ -73,3 +73,18 @@ def test_store_prefill_small_blocks_and_splits():
 def test_store_prefill_full(name):
     case = W.FULL_CASES[name]()
     check(case, oracle_seqs=[0, case.num_seqs // 2, case.num_seqs - 1])
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs", [
+    (8, 8, 128, 64),     # group 1
+    (16, 4, 128, 16),    # group 4, small blocks
+    (16, 2, 128, 32),    # group 8
+    (16, 8, 64, 128),    # head_dim 64
+])
+def test_store_prefill_shapes(hq, hkv, d, bs):
+    """Every GQA group and head_dim, with ragged tails and unaligned cached prefixes."""
+    case = W.prefill_case(f"spshape_{hq}_{hkv}_{d}_{bs}", 5500 + hq + d + bs,
+                          lengths=[1, 5, 64, 65, 130, 300, 700, 257],
+                          cached=[0, 0, 0, 1, 64, 100, 256, 256], hq=hq, hkv=hkv, d=d, bs=bs)
+    check(case)
+    check(case, layout="bhsd", split_keys=128)
