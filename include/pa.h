@@ -211,8 +211,11 @@ int pa_decode(const void* q, int64_t q_seq_stride, int64_t q_head_stride, const 
  * The decode step of [Intro §13.1, §13.2] (store this step's K/V, then
  * attend) for the batch where sequence b has exactly one new token, row b of
  * k_new / v_new, at position context_lens[b] - 1 and slot slot_mapping[b]
- * (-1: no store; such a row is a padding row and must have context_lens[b]
- * = 0).  A row with context_lens[b] = 0 stores nothing, whatever its slot.  The cache rows at those slots afterwards hold the new K/V exactly as
+ * (-1: no store).  A padding row has slot -1 and context_lens[b] = 0; a row
+ * with one of the two and not the other is invalid.  When the fused launch
+ * would keep fewer waves resident than the grid needs while the plain
+ * partition kernel would not, the library stores first in a launch of its
+ * own; the results are the same bits either way.  The cache rows at those slots afterwards hold the new K/V exactly as
  * pa_store_kv writes them, and the workspace holds exactly what pa_decode
  * writes after that store (bit for bit); follow with pa_decode_reduce.
  * slot_mapping[b] must be the slot block_table[b] gives position

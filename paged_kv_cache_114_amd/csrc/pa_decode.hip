@@ -355,9 +355,53 @@ hipError_t pick_nw(const DecodeArgs& a, hipStream_t stream) {
   return run_partition<T, D, G, 1, kStore>(a, stream);
 }
 
+// Waves of kernel K resident at once on the current GPU (0 if the query
+// fails).  The split window's LDS is a few hundred bytes, far below what
+// limits residency, so the answer depends only on the kernel and the device
+// and is kept per device.
+template <auto kKernel>
+int64_t resident_waves(int threads, size_t lds) {
+  constexpr int kMaxDevices = 64;
+  static int64_t known[kMaxDevices] = {};  // 0: not asked yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices && known[dev] > 0) return known[dev];
+  int cus = 0, occ = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kKernel, threads, lds) != hipSuccess)
+    return 0;
+  const int64_t waves = int64_t{occ} * cus * (threads / kWave);
+  if (dev >= 0 && dev < kMaxDevices) known[dev] = waves;
+  return waves;
+}
+
+// The fused store costs the partition kernel registers (fewer waves resident).
+// When the grid fits the GPU at once only without them (a long-context batch
+// such as 512 sequences x 8 kv heads), the store goes first as its own
+// launch and the plain kernel follows; both ways write the same bits.
+template <typename T, int D, int G, int NW>
+hipError_t run_with_store(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t waves = int64_t{a.num_seqs} * a.num_kv_heads * a.num_splits;
+  const size_t lds = ((a.partition_tokens / a.block_size) + 2) * sizeof(int32_t);
+  const int64_t fused = resident_waves<decode_partition_kernel<T, D, G, NW, true>>(NW * kWave, lds);
+  const int64_t plain = resident_waves<decode_partition_kernel<T, D, G, NW, false>>(NW * kWave, lds);
+  if (waves <= fused || waves > plain) return run_partition<T, D, G, NW, true>(a, stream);
+  const StoreArgs sa{a.k_new, a.v_new, a.k_tok_stride, a.k_head_stride, a.v_tok_stride,
+                     a.v_head_stride, const_cast<void*>(a.k_cache),
+                     const_cast<void*>(a.v_cache), a.slot_mapping, a.num_seqs, a.num_kv_heads,
+                     a.head_dim, a.block_size, static_cast<int32_t>(sizeof(T)), a.geom};
+  const hipError_t err = launch_store(sa, stream);
+  if (err != hipSuccess) return err;
+  return run_partition<T, D, G, NW, false>(a, stream);
+}
+
 template <typename T, int D, int G>
 hipError_t pick_store(const DecodeArgs& a, hipStream_t stream) {
-  return a.k_new ? pick_nw<T, D, G, true>(a, stream) : pick_nw<T, D, G, false>(a, stream);
+  if (!a.k_new) return pick_nw<T, D, G, false>(a, stream);
+  if (a.num_kv_heads % 8 == 0) return run_with_store<T, D, G, 8>(a, stream);
+  if (a.num_kv_heads % 4 == 0) return run_with_store<T, D, G, 4>(a, stream);
+  if (a.num_kv_heads % 2 == 0) return run_with_store<T, D, G, 2>(a, stream);
+  return run_with_store<T, D, G, 1>(a, stream);
 }
 
 template <typename T, int D>

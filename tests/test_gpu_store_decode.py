@@ -101,3 +101,12 @@ def test_store_decode_shapes(hq, hkv, d, dtype, bs):
                          dtype=dtype, bs=bs)
     check(case, partition=64)
     check(case, partition=256, layout="bhsd")
+
+
+def test_store_decode_large_batch():
+    """448 sequences x 8 kv heads in one split each: 3,584 waves, more than the fused
+    launch keeps resident on a 256-CU GPU but not more than the plain kernel does, so the
+    library stores in a launch of its own first; the bits are the same either way."""
+    rng = np.random.default_rng(5600)
+    case = W.decode_case("sd_large", 5600, lengths=rng.integers(1, 200, size=448))
+    check(case, partition=256, oracle_seqs=list(range(0, 448, 37)))
