@@ -4,8 +4,8 @@
 A step is one pass of the hot path over one batch of synthetic input: for a
 decode workload, pa_store_decode (this step's K/V rows stored, and the split-K
 partition pass, in one launch) -> pa_decode_reduce; for the prefill workload,
-pa_store_prefill_varlen (the store in the work-list launch, then the tile
-kernel).  The two-call steps (pa_store_kv, then pa_decode -> pa_decode_reduce
+pa_store_prefill_varlen (the work-list launch, then the tile kernel, which
+reads this step's keys from k/v and stores them).  The two-call steps (pa_store_kv, then pa_decode -> pa_decode_reduce
 or pa_prefill_varlen) are reported beside them.  Inputs are resident in HBM before timing starts.  Before
 every step a 1 GiB buffer is read (outside the timed events) so the 256 MB
 Infinity Cache and the L2s hold no KV: a real engine touches 28 layers'
@@ -210,7 +210,7 @@ class Runner:
             mark(4 * k + 2)
             pa.pa_decode_reduce(self.ws, v["context_lens"], self.splits, self.partition,
                                 self.out)
-        elif self.fused_store:  # the store runs in the prefill's work-list launch
+        elif self.fused_store:  # the store runs inside the prefill's tile kernel
             pa.pa_store_prefill_varlen(v["k_new"], v["v_new"], v["slot_mapping"], v["q"],
                                        v["k_cache"], v["v_cache"], v["cu_seqlens_q"],
                                        v["cu_seqlens_k"], v["block_table"], c.max_seqlen_q,

@@ -330,18 +330,24 @@ int pa_prefill_varlen(const void* q, int64_t q_tok_stride, int64_t q_head_stride
 
 /*
  * pa_store_prefill_varlen -- pa_store_kv of this step's new rows and
- * pa_prefill_varlen, with the store done in the same launch as the work-list
- * build.
+ * pa_prefill_varlen in the prefill's own launches.
  *
  * [Intro §13.1, §13.2]: the prefill step stores the new tokens' K/V, then
  * attends over the paged cache.  The new tokens are the query rows: row i of
  * k_new / v_new is query row i's token and goes to slot slot_mapping[i] (-1:
- * not stored), exactly as pa_store_kv writes it.  The output and the pool are
- * bit for bit those of pa_store_kv followed by pa_prefill_varlen.
+ * not stored), exactly as pa_store_kv writes it.  The tile kernel reads the
+ * keys of this step's positions from k_new / v_new rather than from the cache,
+ * and each work item writes the rows of its own query positions to the cache
+ * from the tiles it holds, so no pass of its own stores them.  The output and
+ * the pool are bit for bit those of pa_store_kv followed by pa_prefill_varlen
+ * when each row's slot_mapping entry is the slot its position has in the
+ * sequence's block_table (as an engine's metadata always has it); a row
+ * stored at another slot, or not at all, is still read from k_new / v_new.
  *
  *   k_new, v_new   [total_q, num_kv_heads, head_dim] of dtype, strides
  *                  k_tok_stride / k_head_stride and v_tok_stride /
- *                  v_head_stride (elements, 16-byte aligned rows).
+ *                  v_head_stride (elements, 16-byte aligned rows; token
+ *                  strides of at most 2^23 elements).
  *   slot_mapping   int32 [total_q].
  * Every other argument is as for pa_prefill_varlen; the caches are written,
  * so they are not const here.

@@ -254,8 +254,9 @@ def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tab
 def pa_store_prefill_varlen(k_new, v_new, slot_mapping, q, k_cache, v_cache, cu_seqlens_q,
                             cu_seqlens_k, block_table, max_seqlen_q, max_seqlen_k, scale, out,
                             workspace, split_keys=0, stream=None, layout="bshd") -> None:
-    """Store the query rows' K/V (``[Tq, Hkv, d]``) through ``slot_mapping`` and run the
-    causal varlen prefill, the store in the same launch as the work-list build."""
+    """Store the query rows' K/V (``[Tq, Hkv, d]``, any token and head strides) through
+    ``slot_mapping`` and run the causal varlen prefill; the tile kernel reads these rows
+    from ``k_new`` / ``v_new`` and writes them to the cache itself."""
     nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
     tq, hq, _ = q.shape
     assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 201;  // 0.2.1
 constexpr int64_t kPrefillMaxTableEntries = 8192;  // 32 KB of LDS beside the K/V tile buffers
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -335,6 +335,9 @@ int prefill_common(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
   if (nr.k && (nr.k_tok_stride < 0 || nr.k_head_stride < 0 || nr.v_tok_stride < 0 ||
                nr.v_head_stride < 0))
     return PA_ERR_INVALID_ARG;
+  // the tile kernel reads 64 of this step's rows with 32-bit offsets
+  if (nr.k && (nr.k_tok_stride > (int64_t{1} << 23) || nr.v_tok_stride > (int64_t{1} << 23)))
+    return PA_ERR_UNSUPPORTED;
   if (!(scale > 0.f)) return PA_ERR_INVALID_ARG;  // also rejects NaN
   size_t need = 0;
   int32_t splits = 1;

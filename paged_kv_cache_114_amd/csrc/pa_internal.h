@@ -30,10 +30,6 @@ struct StoreArgs {
   CacheGeom geom;
 };
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
-struct StoreRows;
-// The row-copy description of a store (false: a shape the copy cannot take).
-template <typename W>
-bool store_rows_args(const StoreArgs& a, StoreRows* r);
 
 struct DecodeArgs {
   const void* q;

@@ -50,7 +50,6 @@
 
 #include "pa_common.h"
 #include "pa_internal.h"
-#include "pa_store_rows.h"
 
 namespace pa {
 namespace {
@@ -124,7 +123,20 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-template <int D, int G>
+// This step's K/V rows when the prefill also stores them (kNew): tiles of
+// these positions are read from here rather than from the cache, and each
+// work item writes the rows of its own query positions into the cache.
+struct NewKV {
+  const char* k;                // row (token t, kv head g) at k + t * k_tok_b + g * k_head_b
+  const char* v;
+  int32_t k_tok_b, v_tok_b;     // bytes; 64 rows fit 32-bit offsets (checked on the host)
+  int64_t k_head_b, v_head_b;   // bytes
+  const int32_t* slot_mapping;  // token -> cache slot, -1: not stored
+  uint16_t* k_cache;            // the caches, written
+  uint16_t* v_cache;
+};
+
+template <int D, int G, bool kNew>
 __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_tok_stride, int64_t q_head_stride,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -133,7 +145,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     int32_t bs_log2, float scale_log2, int32_t split_tiles, uint32_t* __restrict__ tickets,
     const int2* __restrict__ items, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int32_t total_q, uint16_t* __restrict__ out, int64_t out_tok_stride,
-    int64_t out_head_stride, int64_t block_stride, int64_t slot_stride, int64_t head_stride) {
+    int64_t out_head_stride, int64_t block_stride, int64_t slot_stride, int64_t head_stride,
+    NewKV nk) {
   using S = PrefillShape<D, G>;
   // Two K/V tile buffers, row-major [key][dim], each row's 16-byte chunks
   // XOR-swizzled (k_swizzle / v_swizzle) so the MFMA operand reads are free
@@ -193,6 +206,16 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
                    16 * ((lane % S::kChunks) ^ k_swizzle<D>(dma_row(i)));
   const uint32_t dma_vlane = (lane / S::kChunks) * row_bytes +
                              16 * ((lane % S::kChunks) ^ v_swizzle<D>(lane / S::kChunks));
+  // The same per-lane chunks at the row strides of this step's K and V rows.
+  uint32_t new_klane[S::kDmaPerWave], new_vlane = 0;
+  if constexpr (kNew) {
+#pragma unroll
+    for (int i = 0; i < S::kDmaPerWave; ++i)
+      new_klane[i] = (lane / S::kChunks) * nk.k_tok_b +
+                     16 * ((lane % S::kChunks) ^ k_swizzle<D>(dma_row(i)));
+    new_vlane = (lane / S::kChunks) * nk.v_tok_b +
+                16 * ((lane % S::kChunks) ^ v_swizzle<D>(lane / S::kChunks));
+  }
 
   // Work entries come from the plan heaviest first, the kv heads of one query
   // tile side by side (they read the same K/V rows, so those DRAM pages are
@@ -263,6 +286,23 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     for (int s = 0; s < S::kSteps; ++s)
       qf[s] = as_bf16x8(row_ok ? load16(qp + 16 * s) : make_uint4(0, 0, 0, 0));
   }
+  // kNew: the item writes the K/V rows of its own positions p0 .. wg_last_pos
+  // that lie in its key range, in the iteration whose tile holds them.  Lane
+  // (piece i) handles tile row dma_row(i) of every tile -- the row its own DMA
+  // brought in -- which is position p0 + ((dma_row(i) - p0) mod 64) + 64 j for
+  // j < kPosPerRow; their slots are loaded here, with the query.
+  constexpr int kPosPerRow = (S::kBM + kBN - 1) / kBN;
+  const int p0 = ctx0 + wg_q0;
+  int32_t st_slot[S::kDmaPerWave][kPosPerRow];
+  if constexpr (kNew) {
+#pragma unroll
+    for (int i = 0; i < S::kDmaPerWave; ++i)
+#pragma unroll
+      for (int j = 0; j < kPosPerRow; ++j) {
+        const int pos = p0 + ((dma_row(i) - p0) & (kBN - 1)) + kBN * j;
+        st_slot[i][j] = pos <= wg_last_pos ? nk.slot_mapping[q_begin + pos - ctx0] : -1;
+      }
+  }
   __syncthreads();  // bt_lds ready
 
   // A tile moves from HBM to LDS by DMA (global_load_lds): a wave-wide
@@ -273,9 +313,25 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // last_pos (a readable row), so P.V only ever multiplies finite values.
   // A lane's row within the tile and its source chunks are the same for every
   // tile.
-  auto dma = [&](const uint16_t* cache, uint16_t* lds, int kt0, auto is_v) {
+  auto dma = [&](uint16_t* lds, int kt0, auto is_v) {
     constexpr bool kV = decltype(is_v)::value;
-    if (tile_in_block && kt0 + kBN - 1 <= last_pos) {
+    const uint16_t* cache = kV ? v_cache : k_cache;
+    if (kNew && kt0 >= ctx0 && kt0 + kBN - 1 <= last_pos) {
+      // a whole tile of this step's rows: consecutive rows of the new K or V
+      const int32_t tok_b = kV ? nk.v_tok_b : nk.k_tok_b;
+      const char* src = (kV ? nk.v : nk.k) + static_cast<int64_t>(q_begin + kt0 - ctx0) * tok_b +
+                        g * (kV ? nk.v_head_b : nk.k_head_b);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(src), 0, 0x7fffffff, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < S::kDmaPerWave; ++i) {
+        const int piece = wave * S::kDmaPerWave + i;
+        lds_void_t* dst = (lds_void_t*)(lds + piece * 512);
+        const uint32_t voff = kV ? new_vlane : new_klane[i];
+        const int soff = piece * S::kRowsPerDma * tok_b;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, soff, 0, 0);
+      }
+    } else if (tile_in_block && kt0 + kBN - 1 <= last_pos && (!kNew || kt0 + kBN - 1 < ctx0)) {
       const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(kt0 >> bs_log2) - first_blk]);
       const int64_t tile_off =
           blk * block_stride + (kt0 & bs_mask) * slot_stride + g * head_stride;
@@ -294,23 +350,69 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
       // Piece by piece: a piece's kRowsPerDma rows lie in one block (block
       // sizes are powers of two of at least 8); rows past last_pos are taken
       // from last_pos, so each piece needs one block-table entry and one
-      // uniform base, and a lane only adds its clamped row.
+      // uniform base, and a lane only adds its clamped row.  With kNew, lanes
+      // whose row is one of this step's (position >= ctx0) read it from the
+      // new rows instead, based at the piece's first such row.
 #pragma unroll
       for (int i = 0; i < S::kDmaPerWave; ++i) {
         const int piece = wave * S::kDmaPerWave + i;
         const int r0 = min(kt0 + piece * S::kRowsPerDma, last_pos);
-        const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(r0 >> bs_log2) - first_blk]);
-        const int64_t row_off =
-            blk * block_stride + (r0 & bs_mask) * slot_stride + g * head_stride;
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(cache + row_off), 0, 0x7fffffff, kBufferFlags);
         const int lane_row = lane / S::kChunks;
         const int dr = min(lane_row, last_pos - r0);
-        const uint32_t off = (kV ? dma_vlane : dma_klane[i]) + (dr - lane_row) * row_bytes;
         lds_void_t* dst = (lds_void_t*)(lds + piece * 512);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off, 0, 0, 0);
+        if (kNew && r0 + dr >= ctx0) {
+          const int n0 = max(r0, ctx0);
+          const int32_t tok_b = kV ? nk.v_tok_b : nk.k_tok_b;
+          const char* src = (kV ? nk.v : nk.k) + static_cast<int64_t>(q_begin + n0 - ctx0) * tok_b +
+                            g * (kV ? nk.v_head_b : nk.k_head_b);
+          const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<char*>(src), 0, 0x7fffffff, kBufferFlags);
+          const uint32_t off = (kV ? new_vlane : new_klane[i]) + (r0 + dr - n0 - lane_row) * tok_b;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off, 0, 0, 0);
+        } else {
+          const int blk = __builtin_amdgcn_readfirstlane(bt_lds[(r0 >> bs_log2) - first_blk]);
+          const int64_t row_off =
+              blk * block_stride + (r0 & bs_mask) * slot_stride + g * head_stride;
+          const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<uint16_t*>(cache + row_off), 0, 0x7fffffff, kBufferFlags);
+          const uint32_t off = (kV ? dma_vlane : dma_klane[i]) + (dr - lane_row) * row_bytes;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off, 0, 0, 0);
+        }
       }
     }
+  };
+
+  // kNew: write the rows of this item's positions that the tile in k_src /
+  // v_src holds (tile kt) to their slots.  Each lane reads back the 16 bytes
+  // its own DMA placed and stores them at the source chunk they came from.
+  auto store_tile = [&](const uint16_t* k_src, const uint16_t* v_src, int kt) {
+    // Everything lane-dependent is derived here from an opaque copy of the
+    // lane index, so the compiler cannot hoist it out of the key loop and hold
+    // it in registers for the whole loop (it did: 40 more VGPRs).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < S::kDmaPerWave; ++i)
+#pragma unroll
+      for (int j = 0; j < kPosPerRow; ++j) {
+        const int piece = wave * S::kDmaPerWave + i;
+        const int trow = piece * S::kRowsPerDma + ln / S::kChunks;  // dma_row(i)
+        const int pos = p0 + ((trow - p0) & (kBN - 1)) + kBN * j;
+        int slot = st_slot[i][j];
+        asm volatile("" : "+v"(slot));
+        if ((pos >> 6) == kt && slot >= 0) {  // slot -1 also past wg_last_pos
+          const uint4 kd = *reinterpret_cast<const uint4*>(k_src + piece * 512 + ln * 8);
+          const uint4 vd = *reinterpret_cast<const uint4*>(v_src + piece * 512 + ln * 8);
+          const int64_t row = (slot >> bs_log2) * block_stride + (slot & bs_mask) * slot_stride +
+                              g * head_stride;
+          *reinterpret_cast<uint4*>(nk.k_cache + row +
+                                    8 * ((ln % S::kChunks) ^ k_swizzle<D>(trow))) = kd;
+          *reinterpret_cast<uint4*>(nk.v_cache + row +
+                                    8 * ((ln % S::kChunks) ^ v_swizzle<D>(ln / S::kChunks))) = vd;
+        }
+        // one row at a time: the tile loop's registers are nearly all taken
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
 
   f32x16_t acc_o[S::kDB];
@@ -483,16 +585,19 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     if (tid == 0 && kt + 1 == kt_end)
       next_entry = static_cast<int>(gridDim.x + atomicAdd(tickets, 1u));
     if (kt + 1 < kt_end) {
-      dma(k_cache, k_nxt, kt0 + kBN, std::false_type{});
-      dma(v_cache, v_nxt, kt0 + kBN, std::true_type{});
+      dma(k_nxt, kt0 + kBN, std::false_type{});
+      dma(v_nxt, kt0 + kBN, std::true_type{});
     }
+    // the stores complete while the tile is multiplied (waited for below)
+    if constexpr (kNew)
+      if (kt0 <= wg_last_pos && kt0 + kBN > p0) store_tile(k_cur, v_cur, kt);
     if (kt0 <= w_last_pos) compute(k_cur, v_cur, kt0, with_rest);  // else: all in this wave's future
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  dma(k_cache, k_lds0, kt_begin * kBN, std::false_type{});
-  dma(v_cache, v_lds0, kt_begin * kBN, std::true_type{});
+  dma(k_lds0, kt_begin * kBN, std::false_type{});
+  dma(v_lds0, kt_begin * kBN, std::true_type{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // One loop per kind of wave (the waves of a workgroup may run different
@@ -678,25 +783,6 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   plan_body<BM>(cu_q, cu_k, num_seqs, split_tiles, num_kv_heads, tickets, items, merges);
 }
 
-// The work list and this step's KV store in one launch: workgroup 0 builds
-// the list while the others copy the new rows into the cache.  Both must be
-// done before the tile kernel starts, which stream order gives; one launch
-// instead of two removes a launch and lets the list build overlap the copy.
-template <int BM>
-__global__ __launch_bounds__(kPlanThreads) void prefill_plan_store_kernel(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
-    int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
-    int2* __restrict__ items, int2* __restrict__ merges, StoreRows store) {
-  if (blockIdx.x == 0) {
-    plan_body<BM>(cu_q, cu_k, num_seqs, split_tiles, num_kv_heads, tickets, items, merges);
-    return;
-  }
-  constexpr int kWaves = kPlanThreads / kWave;
-  store_rows<uint4>(store,
-                    (blockIdx.x - 1) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave),
-                    (gridDim.x - 1) * kWaves);
-}
-
 // Merge of the key-range partials of split query tiles ([Intro §9.5]: each
 // partial carries its own maximum m_s and sum l_s, so the output is
 // sum_s 2^(m_s - m*) acc_s / sum_s 2^(m_s - m*) l_s with m* = max_s m_s).
@@ -772,28 +858,16 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   }
 }
 
-template <int D, int G>
-hipError_t run(const PrefillArgs& a, hipStream_t stream) {
+template <int D, int G, bool kNew>
+hipError_t run(const PrefillArgs& a, const NewKV& nk, hipStream_t stream) {
   using S = PrefillShape<D, G>;
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
   const size_t bt_bytes = static_cast<size_t>((a.max_seqlen_k + a.block_size - 1) >> bs_log2) * 4;
   // split_tiles >= every tile's key-tile count when nothing is split
   const int split_tiles = a.num_splits > 1 ? a.split_keys / kBN : (a.max_seqlen_k + kBN - 1) / kBN;
-  if (a.store) {
-    StoreRows rows;
-    if (!store_rows_args<uint4>(*a.store, &rows)) return hipErrorInvalidValue;
-    constexpr int kWaves = kPlanThreads / kWave;
-    const int64_t want = (int64_t{rows.rows} + kWaves - 1) / kWaves;
-    const int store_blocks = static_cast<int>(want < 4096 ? want : 4096);
-    hipLaunchKernelGGL((prefill_plan_store_kernel<S::kBM>), dim3(1 + store_blocks),
-                       dim3(kPlanThreads), 0, stream, a.cu_seqlens_q, a.cu_seqlens_k,
-                       a.num_seqs, split_tiles, a.num_kv_heads, a.tickets, a.items, a.merges,
-                       rows);
-  } else {
-    hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
-                       a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, split_tiles, a.num_kv_heads,
-                       a.tickets, a.items, a.merges);
-  }
+  hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
+                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, split_tiles, a.num_kv_heads,
+                     a.tickets, a.items, a.merges);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // one workgroup per resident slot: they stay until the work list is empty
@@ -801,17 +875,18 @@ hipError_t run(const PrefillArgs& a, hipStream_t stream) {
   if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
   if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
     return err;
-  if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<D, G>, S::kThreads,
-                                                          bt_bytes)) != hipSuccess)
+  if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<D, G, kNew>,
+                                                          S::kThreads, bt_bytes)) != hipSuccess)
     return err;
   occ = occ > 0 ? occ : 1;
-  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(cus * occ), dim3(S::kThreads), bt_bytes, stream,
-                     static_cast<const uint16_t*>(a.q), a.q_tok_stride, a.q_head_stride,
+  hipLaunchKernelGGL((prefill_kernel<D, G, kNew>), dim3(cus * occ), dim3(S::kThreads), bt_bytes,
+                     stream, static_cast<const uint16_t*>(a.q), a.q_tok_stride, a.q_head_stride,
                      static_cast<const uint16_t*>(a.k_cache), static_cast<const uint16_t*>(a.v_cache),
                      a.cu_seqlens_q, a.cu_seqlens_k, a.block_table, a.block_table_stride,
                      a.num_kv_heads, bs_log2, a.scale * kLog2e, split_tiles, a.tickets, a.items,
                      a.ws_acc, a.ws_ml, a.total_q, static_cast<uint16_t*>(a.out),
-                     a.out_tok_stride, a.out_head_stride, a.geom.block, a.geom.slot, a.geom.head);
+                     a.out_tok_stride, a.out_head_stride, a.geom.block, a.geom.slot, a.geom.head,
+                     nk);
   err = hipGetLastError();
   if (err != hipSuccess || a.num_splits == 1) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(4 * cus), dim3(256), 0, stream,
@@ -819,6 +894,21 @@ hipError_t run(const PrefillArgs& a, hipStream_t stream) {
                      a.ws_acc, a.ws_ml, a.total_q, split_tiles, static_cast<uint16_t*>(a.out),
                      a.out_tok_stride, a.out_head_stride);
   return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t run(const PrefillArgs& a, hipStream_t stream) {
+  if (!a.store) return run<D, G, false>(a, NewKV{}, stream);
+  // This step's rows: the tile kernel reads them from k / v and stores them.
+  const StoreArgs& st = *a.store;
+  const int64_t kt = st.k_tok_stride * 2, vt = st.v_tok_stride * 2;
+  // lane offsets within a 64-row tile of the new rows are 32-bit
+  if (kt > (int64_t{1} << 24) || vt > (int64_t{1} << 24)) return hipErrorInvalidValue;
+  const NewKV nk{static_cast<const char*>(st.k), static_cast<const char*>(st.v),
+                 static_cast<int32_t>(kt), static_cast<int32_t>(vt), st.k_head_stride * 2,
+                 st.v_head_stride * 2, st.slot_mapping, static_cast<uint16_t*>(st.k_cache),
+                 static_cast<uint16_t*>(st.v_cache)};
+  return run<D, G, true>(a, nk, stream);
 }
 
 template <int D>

@@ -20,8 +20,7 @@ __global__ __launch_bounds__(kStoreWaves* kWave) void store_kernel(StoreRows a) 
                 gridDim.x * kStoreWaves);
 }
 
-}  // namespace
-
+// The row-copy description of a store (false: a shape the copy cannot take).
 template <typename W>
 bool store_rows_args(const StoreArgs& a, StoreRows* r) {
   const int64_t eb = a.elt_bytes;
@@ -39,9 +38,6 @@ bool store_rows_args(const StoreArgs& a, StoreRows* r) {
                  a.geom.slot * eb, a.geom.head * eb};
   return true;
 }
-template bool store_rows_args<uint4>(const StoreArgs&, StoreRows*);
-
-namespace {
 
 template <typename W>
 hipError_t run(const StoreArgs& a, hipStream_t stream) {

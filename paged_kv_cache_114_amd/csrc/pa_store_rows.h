@@ -1,5 +1,4 @@
-// The KV store's row copy, shared by the store kernel and by the prefill's
-// combined work-list + store launch.
+// The KV store's row copy (the body of the store kernel).
 //
 // [Intro §13.1] ("大模型推理入门与 nano-vLLM 源码详解"): each new token's K and V
 // rows for all kv heads are copied into slot slot_mapping[i] of this layer's

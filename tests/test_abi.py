@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert pa.version() == 200
+    assert pa.version() == 201
     assert pa.strerror(pa.PA_OK) == "ok"
     for code in (pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED, pa.PA_ERR_WORKSPACE,
                  pa.PA_ERR_LAUNCH):
@@ -196,6 +196,23 @@ def test_prefill_split_validation():
     assert prefill(b=5000, ws=fake, wsb=big, **ptrs) == pa.PA_ERR_UNSUPPORTED    # > 4096 seqs
     assert prefill(sk=64, bs=8, mk=8 * 65536, mq=8 * 8192, tq=8 * 8192, ws=fake, wsb=big,
                    **ptrs) == pa.PA_ERR_UNSUPPORTED                  # > 32767 key ranges
+
+
+def store_prefill(kt=1024, vt=1024):
+    """pa_store_prefill_varlen with fake pointers and this step's rows at token
+    strides kt / vt (elements); the checks run before anything is enqueued."""
+    fake = ctypes.c_void_p(256)
+    return pa.library().pa_store_prefill_varlen(
+        fake, fake, kt, 128, vt, 128, fake, fake, 2048, 128, fake, fake, fake, fake, fake, 8, 8,
+        6000, 16, 8, 128, 256, 64, 0, 2048, 2048, 0.088, 0, fake, 1 << 40, fake, 2048, 128, BF16,
+        NULL)
+
+
+def test_store_prefill_new_row_stride_limit():
+    """The tile kernel reads 64 of this step's rows with 32-bit lane offsets."""
+    assert store_prefill(kt=1 << 24) == pa.PA_ERR_UNSUPPORTED
+    assert store_prefill(vt=(1 << 23) + 8) == pa.PA_ERR_UNSUPPORTED
+    assert store_prefill(kt=-8) == pa.PA_ERR_INVALID_ARG
 
 
 def rope(**kw):

@@ -137,7 +137,7 @@ def test_graph_prefill_step_replays_equal_eager(fused):
 
         def step():
             for lay in layers:
-                if fused:  # the store in the work-list launch
+                if fused:  # the store inside the tile kernel
                     pa.pa_store_prefill_varlen(
                         lay["k_new"], lay["v_new"], lay["slot_mapping"], lay["q"],
                         lay["k_cache"], lay["v_cache"], lay["cu_seqlens_q"], lay["cu_seqlens_k"],

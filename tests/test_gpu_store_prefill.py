@@ -1,4 +1,4 @@
-"""pa_store_prefill_varlen (this step's rows stored in the work-list launch) against the
+"""pa_store_prefill_varlen (this step's rows read from k/v and stored by the tile kernel) against the
 two-call path pa_store_kv + pa_prefill_varlen, bit for bit, and against the oracle."""
 
 import numpy as np
@@ -88,3 +88,32 @@ def test_store_prefill_shapes(hq, hkv, d, bs):
                           cached=[0, 0, 0, 1, 64, 100, 256, 256], hq=hq, hkv=hkv, d=d, bs=bs)
     check(case)
     check(case, layout="bhsd", split_keys=128)
+
+
+def test_store_prefill_strided_new_rows():
+    """k / v as views into one fused projection row ([T, (Hq + 2 Hkv) d]), so their
+    token stride is not Hkv * d and differs from the cache's: the tile kernel reads
+    this step's rows from these views and must match the two-call path on
+    contiguous copies, bit for bit."""
+    case = W.prefill_case("sp_strided", 5600, lengths=[1, 70, 300, 129], cached=[0, 3, 256, 64])
+    vals = W.materialize(case, DEV)
+    t, hq, hkv, d = case.num_new_tokens, case.num_q_heads, case.num_kv_heads, case.head_dim
+    qkv = torch.full((t, (hq + 2 * hkv) * d + 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    k_view = qkv[:, hq * d:(hq + hkv) * d].view(t, hkv, d)
+    v_view = qkv[:, (hq + hkv) * d:(hq + 2 * hkv) * d].view(t, hkv, d)
+    k_view.copy_(vals["k_new"])
+    v_view.copy_(vals["v_new"])
+    assert k_view.stride(0) == (hq + 2 * hkv) * d + 64
+    print(f"store_prefill strided T={t} tok_stride={k_view.stride(0)}", flush=True)
+
+    kc, vc = vals["k_cache"].clone(), vals["v_cache"].clone()
+    out_f = torch.full_like(vals["q"], float("nan"))
+    args = (vals["cu_seqlens_q"], vals["cu_seqlens_k"], vals["block_table"], case.max_seqlen_q,
+            case.max_context_len, case.scale)
+    pa.pa_store_prefill_varlen(k_view, v_view, vals["slot_mapping"], vals["q"], kc, vc, *args,
+                               out_f, prefill_workspace(case))
+    out_s, kc_s, vc_s = run(case, vals, False, "bshd", 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), "strided fused != two-call"
+    assert torch.equal(kc.view(torch.int16), kc_s.view(torch.int16)), "K pool"
+    assert torch.equal(vc.view(torch.int16), vc_s.view(torch.int16)), "V pool"
