@@ -41,8 +41,12 @@
 //   reference maximum by more than 8 in base-2 units (lazy rescaling);
 //   otherwise the probabilities are taken against the old reference and stay
 //   below 2^8.
-// * Query tiles are dispatched heaviest first: blockIdx.z counts tiles back
-//   from the end of each sequence, and the last tiles see the most keys.
+// * Work items (sequence, query tile, key range, kv head) come from a list
+//   built on the device by one workgroup, heaviest first; a fixed set of
+//   workgroups, one per resident slot, takes them from a counter.
+// * With the step's store (kNew), keys at this step's positions are read from
+//   the new K/V rows instead of the cache, and each item writes the rows of
+//   its own query positions to the cache from the tiles it holds in LDS.
 
 #include <math.h>
 
