@@ -294,9 +294,12 @@ int pa_prefill_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_h
  * (store this step's K/V first).  With c = Lk - Lq cached positions, query row
  * i sits at position c + i and attends to positions 0..c+i (a causal mask
  * aligned to the bottom-right).  Scores are scale * q.k in fp32; the softmax
- * runs online in fp32; both matrix products run on bf16 MFMA tiles, the
- * probabilities entering P.V as a bf16 head plus a bf16 remainder (about 16
- * significant bits).
+ * runs online in fp32; both matrix products run on bf16 MFMA tiles.  The
+ * probabilities enter P.V rounded to nearest bf16 (8 significant bits), except
+ * for a block of 32 query rows whose first row sees fewer than 256 keys: there
+ * they enter as a truncated bf16 head plus the bf16 remainder (about 16
+ * significant bits), because with few keys the weight sits on a few values
+ * and bf16 rounding alone can exceed the stated error bound.
  *
  *   q, out        [total_q, num_q_heads, head_dim] (total_q = cu_seqlens_q[num_seqs]),
  *                 strides q_tok_stride / q_head_stride, out_tok_stride /

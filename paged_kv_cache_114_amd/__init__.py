@@ -147,9 +147,28 @@ def _cache_shape(cache, layout):
     return nb, bs, hkv, d, code
 
 
+def _check_pool(k_cache, v_cache, *same_dtype):
+    """The library derives a cache's strides from its shape, so both caches must be
+    contiguous, of one shape and of the dtype of every other float tensor passed."""
+    assert k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous"
+    assert k_cache.shape == v_cache.shape, "k_cache and v_cache shapes differ"
+    for t in (v_cache, *same_dtype):
+        if t is not None:
+            assert t.dtype == k_cache.dtype, f"dtype {t.dtype} differs from the cache's {k_cache.dtype}"
+
+
+def _check_table(block_table, block_size, max_len):
+    """Every row must have a column for each block a sequence of max_len tokens uses."""
+    assert block_table.dim() == 2 and block_table.stride(1) == 1, "block_table must be [B, W]"
+    assert block_table.shape[1] * block_size >= max_len, (
+        f"block_table has {block_table.shape[1]} columns, fewer than "
+        f"ceil({max_len} / {block_size})")
+
+
 def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None, layout="bshd") -> None:
     """Store this step's K/V rows ``[T, Hkv, d]`` into the paged caches."""
     nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    _check_pool(k_cache, v_cache, k, v)
     assert k.stride(-1) == 1 and v.stride(-1) == 1, "innermost stride must be 1"
     _check("pa_store_kv", library().pa_store_kv(
         _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1), _ptr(k_cache),
@@ -165,6 +184,7 @@ def pa_qk_norm_rope_store(qkv, q_norm_weight, k_norm_weight, positions, slot_map
     Both norm weights ``None``: rotation only."""
     nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
     assert hkv == num_kv_heads, "cache head count differs from num_kv_heads"
+    _check_pool(k_cache, v_cache, qkv, q_out, q_norm_weight, k_norm_weight)
     assert qkv.stride(-1) == 1 and q_out.stride(-1) == 1, "innermost stride must be 1"
     assert q_out.dim() == 3 and q_out.stride(1) == d, "q_out must be [T, Hq, d] with head stride d"
     _check("pa_qk_norm_rope_store", library().pa_qk_norm_rope_store(
@@ -189,6 +209,8 @@ def pa_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len, p
               scale, workspace, stream=None, layout="bshd") -> None:
     """Partition pass: ``q [B, Hq, d]``; fills ``workspace`` (a float32 device tensor)."""
     nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    _check_pool(k_cache, v_cache, q)
+    _check_table(block_table, bs, max_context_len)
     b, hq, _ = q.shape
     _check("pa_decode", library().pa_decode(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
@@ -203,6 +225,8 @@ def pa_store_decode(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_table
     """Store each sequence's new K/V row (``[B, Hkv, d]``, at position ``context_lens - 1``)
     through ``slot_mapping`` and run the partition pass, in one launch."""
     nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    _check_pool(k_cache, v_cache, q, k_new, v_new)
+    _check_table(block_table, bs, max_context_len)
     b, hq, _ = q.shape
     assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"
     _check("pa_store_decode", library().pa_store_decode(
@@ -241,6 +265,8 @@ def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tab
     ``workspace``: a device tensor of at least pa_prefill_workspace_size bytes for the
     same sizes and ``split_keys`` (> 0 cuts long query tiles' key loops)."""
     nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    _check_pool(k_cache, v_cache, q, out)
+    _check_table(block_table, bs, max_seqlen_k)
     tq, hq, _ = q.shape
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("pa_prefill_varlen", library().pa_prefill_varlen(
@@ -258,6 +284,8 @@ def pa_store_prefill_varlen(k_new, v_new, slot_mapping, q, k_cache, v_cache, cu_
     ``slot_mapping`` and run the causal varlen prefill; the tile kernel reads these rows
     from ``k_new`` / ``v_new`` and writes them to the cache itself."""
     nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    _check_pool(k_cache, v_cache, q, out, k_new, v_new)
+    _check_table(block_table, bs, max_seqlen_k)
     tq, hq, _ = q.shape
     assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"
     ws_bytes = workspace.numel() * workspace.element_size()

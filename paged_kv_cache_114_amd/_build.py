@@ -35,22 +35,50 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source into libpa.so; returns its path.  Always recompiles."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *srcs,
-           "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
+    return res.returncode, msgs
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source into libpa.so; returns its path.  Always recompiles.
+
+    Each source becomes an object of its own (in parallel, they share no device
+    code), then one link makes the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for s in SOURCES:
+        obj = os.path.join(obj_dir, os.path.splitext(s)[0] + ".o")
+        jobs.append((obj, [hipcc(), *compile_flags, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
+                           "-c", os.path.join(CSRC, s), "-o", obj]))
+    if verbose:
+        for _, cmd in jobs:
+            print(" ".join(cmd), flush=True)
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as pool:
+        results = list(pool.map(lambda j: _run(j[1]), jobs))
+    failed = False
+    for (obj, _), (rc, msgs) in zip(jobs, results):
+        if rc != 0:
+            failed = True
+            sys.stderr.write("\n".join(msgs) + "\n")
+        elif verbose and msgs:
+            print("\n".join(msgs))
+    if failed:
+        raise RuntimeError("hipcc failed")
+    tmp = LIB + ".tmp"
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, msgs = _run(link)
+    if rc != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
-    if verbose and msgs:
-        print("\n".join(msgs))
+        raise RuntimeError(f"hipcc link failed ({rc})")
     os.replace(tmp, LIB)
     return LIB
 

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, int64_t bt_stride,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_kv_heads,
-    int32_t bs_log2, int32_t bt_entries, int32_t partition_tokens, int32_t num_splits,
+    int32_t bs_log2, int32_t max_ctx, int32_t partition_tokens, int32_t num_splits,
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t block_stride,
     int32_t slot_stride, int64_t head_stride, const T* k_new, const T* v_new, int64_t k_tok_stride,
     int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
@@ -85,6 +85,8 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
   // The context length, the split's block-table window and the query are
   // independent loads, issued together: the window is the most a split can
   // touch, clipped to the bt_entries columns every table row has.
+  // Every block-table row has the bt_entries columns a max_ctx-token context uses.
+  const int bt_entries = (max_ctx + (1 << bs_log2) - 1) >> bs_log2;
   const int first_blk = t0 >> bs_log2;
   const int win = min((partition_tokens >> bs_log2) + 2, bt_entries - first_blk);
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * bt_stride + first_blk;
@@ -103,7 +105,9 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     k_new_raw = load16(k_new + b * k_tok_stride + g * k_head_stride + col * kE);
     v_new_raw = load16(v_new + b * v_tok_stride + g * v_head_stride + col * kE);
   }
-  const int ctx = context_lens[b];
+  // A context longer than max_ctx (a caller error) is cut to it, so no split reads
+  // past the staged window.
+  const int ctx = min(context_lens[b], max_ctx);
   if (t0 >= ctx) return;  // empty split (uniform over the workgroup): nothing written
   const int t1 = min(t0 + partition_tokens, ctx);
   const int bs_mask = (1 << bs_log2) - 1;
@@ -331,13 +335,12 @@ template <typename T, int D, int G, int NW, bool kStore>
 hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
   const int max_blk = (a.partition_tokens >> bs_log2) + 2;
-  const int bt_entries = (a.max_context_len + a.block_size - 1) >> bs_log2;
   dim3 grid(a.num_seqs, a.num_kv_heads / NW, a.num_splits);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, NW, kStore>), grid, dim3(NW * kWave),
                      max_blk * sizeof(int32_t), stream, static_cast<const T*>(a.q),
                      a.q_seq_stride, a.q_head_stride, static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_table, a.block_table_stride,
-                     a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, bt_entries,
+                     a.context_lens, a.num_seqs, a.num_kv_heads, bs_log2, a.max_context_len,
                      a.partition_tokens, a.num_splits, a.scale * kLog2e, a.ws_acc, a.ws_ml,
                      static_cast<uint32_t>(a.geom.block), static_cast<int32_t>(a.geom.slot),
                      a.geom.head, static_cast<const T*>(a.k_new), static_cast<const T*>(a.v_new),

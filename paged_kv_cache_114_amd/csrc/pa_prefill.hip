@@ -146,7 +146,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_table, int64_t bt_stride, int32_t num_kv_heads,
-    int32_t bs_log2, float scale_log2, int32_t split_tiles, uint32_t* __restrict__ tickets,
+    int32_t bs_log2, int32_t max_seqlen_k, float scale_log2, int32_t split_tiles,
+    uint32_t* __restrict__ tickets,
     const int2* __restrict__ items, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int32_t total_q, uint16_t* __restrict__ out, int64_t out_tok_stride,
     int64_t out_head_stride, int64_t block_stride, int64_t slot_stride, int64_t head_stride,
@@ -242,8 +243,10 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   const int qt = item.y & 0xffff;
   const int split = item.y >> 16;
   const int q_begin = cu_q[b];
-  const int lq = cu_q[b + 1] - q_begin;
-  const int lk = cu_k[b + 1] - cu_k[b];
+  // lengths as the plan kernel reads them: an Lk above max_seqlen_k (or Lq above
+  // Lk) is a caller error, cut here so no key past the staged table is read
+  const int lk = min(cu_k[b + 1] - cu_k[b], max_seqlen_k);
+  const int lq = min(cu_q[b + 1] - q_begin, lk);
   const int ctx0 = lk - lq;                                 // cached positions
   const int wg_q0 = qt * S::kBM;                            // first query row of the tile
   const int wg_last_pos = ctx0 + min(lq, wg_q0 + S::kBM) - 1;
@@ -664,7 +667,7 @@ constexpr int kPlanBins = 1024;  // weights >= kPlanBins - 1 share the last bin
 template <int BM>
 __device__ __forceinline__ void plan_body(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
-    int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
+    int32_t max_seqlen_k, int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
     int2* __restrict__ items, int2* __restrict__ merges) {
   __shared__ int tile_start[kPrefillPlanMaxSeqs + 1];  // first query-tile index per sequence
   __shared__ int n_merges;
@@ -718,9 +721,11 @@ __device__ __forceinline__ void plan_body(
     const int b = tid * kPer + k;
     n_local[k] = 0;
     if (b < num_seqs) {
-      const int lq = cu_q[b + 1] - cu_q[b];
+      // lengths cut as the tile kernel cuts them
+      const int lk = min(cu_k[b + 1] - cu_k[b], max_seqlen_k);
+      const int lq = min(cu_q[b + 1] - cu_q[b], lk);
       seq_lq[b] = lq;
-      seq_ctx0[b] = cu_k[b + 1] - cu_k[b] - lq;
+      seq_ctx0[b] = lk - lq;
       n_local[k] = (lq + BM - 1) / BM;
     }
     sum += n_local[k];
@@ -782,9 +787,10 @@ __device__ __forceinline__ void plan_body(
 template <int BM>
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
-    int32_t split_tiles, int32_t num_kv_heads, uint32_t* __restrict__ tickets,
-    int2* __restrict__ items, int2* __restrict__ merges) {
-  plan_body<BM>(cu_q, cu_k, num_seqs, split_tiles, num_kv_heads, tickets, items, merges);
+    int32_t max_seqlen_k, int32_t split_tiles, int32_t num_kv_heads,
+    uint32_t* __restrict__ tickets, int2* __restrict__ items, int2* __restrict__ merges) {
+  plan_body<BM>(cu_q, cu_k, num_seqs, max_seqlen_k, split_tiles, num_kv_heads, tickets, items,
+                merges);
 }
 
 // Merge of the key-range partials of split query tiles ([Intro §9.5]: each
@@ -805,7 +811,7 @@ struct MergeShape {
 template <int D, int G>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_kv_heads,
-    const uint32_t* __restrict__ tickets, const int2* __restrict__ merges,
+    int32_t max_seqlen_k, const uint32_t* __restrict__ tickets, const int2* __restrict__ merges,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int32_t total_q,
     int32_t split_tiles, uint16_t* __restrict__ out, int64_t out_tok_stride,
     int64_t out_head_stride) {
@@ -822,8 +828,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   const int b = tile.x;
   const int qt = tile.y;
   const int q_begin = cu_q[b];
-  const int lq = cu_q[b + 1] - q_begin;
-  const int lk = cu_k[b + 1] - cu_k[b];
+  const int lk = min(cu_k[b + 1] - cu_k[b], max_seqlen_k);
+  const int lq = min(cu_q[b + 1] - q_begin, lk);
   const int wg_q0 = qt * S::kBM;
   const int wg_last_pos = lk - lq + min(lq, wg_q0 + S::kBM) - 1;
   const int n_split = (wg_last_pos / kBN + split_tiles) / split_tiles;
@@ -862,6 +868,44 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   }
 }
 
+// Workgroups of the tile kernel resident per CU, and in total, on the current
+// device.  The answer depends on the kernel, its LDS (the block-table stage,
+// sized from max_seqlen_k) and the device; it is asked of the runtime once per
+// device and LDS size.
+template <int D, int G, bool kNew>
+int resident_per_cu(size_t lds) {
+  constexpr int kMaxDevices = 64, kMaxLds = 64;
+  static int known[kMaxDevices][kMaxLds] = {};  // 0: not asked yet; indexed by lds / 512
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  const size_t li = lds / 512;
+  const bool cache = dev >= 0 && dev < kMaxDevices && li < kMaxLds;
+  if (cache && known[dev][li] > 0) return known[dev][li];
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<D, G, kNew>,
+                                                   PrefillShape<D, G>::kThreads, lds) != hipSuccess)
+    return 1;
+  occ = occ > 0 ? occ : 1;
+  if (cache) known[dev][li] = occ;
+  return occ;
+}
+
+template <int D, int G, bool kNew>
+int resident_slots(size_t lds, hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static int cus_known[kMaxDevices] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return 0;
+  int cus = dev >= 0 && dev < kMaxDevices ? cus_known[dev] : 0;
+  if (cus == 0) {
+    *err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (*err != hipSuccess) return 0;
+    if (dev >= 0 && dev < kMaxDevices) cus_known[dev] = cus;
+  }
+  return cus * resident_per_cu<D, G, kNew>(lds);
+}
+
 template <int D, int G, bool kNew>
 hipError_t run(const PrefillArgs& a, const NewKV& nk, hipStream_t stream) {
   using S = PrefillShape<D, G>;
@@ -870,31 +914,28 @@ hipError_t run(const PrefillArgs& a, const NewKV& nk, hipStream_t stream) {
   // split_tiles >= every tile's key-tile count when nothing is split
   const int split_tiles = a.num_splits > 1 ? a.split_keys / kBN : (a.max_seqlen_k + kBN - 1) / kBN;
   hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
-                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, split_tiles, a.num_kv_heads,
-                     a.tickets, a.items, a.merges);
+                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, a.max_seqlen_k, split_tiles,
+                     a.num_kv_heads, a.tickets, a.items, a.merges);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // one workgroup per resident slot: they stay until the work list is empty
-  int dev = 0, cus = 0, occ = 0;
-  if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
-  if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-    return err;
-  if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<D, G, kNew>,
-                                                          S::kThreads, bt_bytes)) != hipSuccess)
-    return err;
-  occ = occ > 0 ? occ : 1;
-  hipLaunchKernelGGL((prefill_kernel<D, G, kNew>), dim3(cus * occ), dim3(S::kThreads), bt_bytes,
+  const int slots = resident_slots<D, G, kNew>(bt_bytes, &err);
+  if (err != hipSuccess) return err;
+  const int cus = slots / cmax(1, resident_per_cu<D, G, kNew>(bt_bytes));
+  hipLaunchKernelGGL((prefill_kernel<D, G, kNew>), dim3(slots), dim3(S::kThreads), bt_bytes,
                      stream, static_cast<const uint16_t*>(a.q), a.q_tok_stride, a.q_head_stride,
                      static_cast<const uint16_t*>(a.k_cache), static_cast<const uint16_t*>(a.v_cache),
                      a.cu_seqlens_q, a.cu_seqlens_k, a.block_table, a.block_table_stride,
-                     a.num_kv_heads, bs_log2, a.scale * kLog2e, split_tiles, a.tickets, a.items,
+                     a.num_kv_heads, bs_log2, a.max_seqlen_k, a.scale * kLog2e, split_tiles,
+                     a.tickets, a.items,
                      a.ws_acc, a.ws_ml, a.total_q, static_cast<uint16_t*>(a.out),
                      a.out_tok_stride, a.out_head_stride, a.geom.block, a.geom.slot, a.geom.head,
                      nk);
   err = hipGetLastError();
   if (err != hipSuccess || a.num_splits == 1) return err;
   hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(4 * cus), dim3(256), 0, stream,
-                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_kv_heads, a.tickets, a.merges,
+                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_kv_heads, a.max_seqlen_k, a.tickets,
+                     a.merges,
                      a.ws_acc, a.ws_ml, a.total_q, split_tiles, static_cast<uint16_t*>(a.out),
                      a.out_tok_stride, a.out_head_stride);
   return hipGetLastError();

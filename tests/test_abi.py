@@ -274,3 +274,33 @@ def test_header_is_c_and_a_c_program_links_the_library(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "all checks passed" in run.stdout
+
+
+def test_binding_checks_cache_shape_dtype_and_table_width():
+    """The binding rejects, before any call into the library, what the library cannot
+    see from pointers and sizes: non-contiguous caches (strides are derived from the
+    shape), mixed dtypes, and block tables narrower than the longest context needs.
+    CPU tensors: every rejected call stops at an assertion."""
+    import torch
+    kc = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    q = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 2), dtype=torch.int32)
+    ctx = torch.ones(1, dtype=torch.int32)
+    ws = torch.zeros(1024, dtype=torch.float32)
+    with pytest.raises(AssertionError, match="contiguous"):
+        pa.pa_decode(q, kc.transpose(1, 2).contiguous().transpose(1, 2), vc, bt, ctx, 32, 64,
+                     0.125, ws)
+    with pytest.raises(AssertionError, match="dtype"):
+        pa.pa_decode(q.float(), kc, vc, bt, ctx, 32, 64, 0.125, ws)
+    with pytest.raises(AssertionError, match="dtype"):
+        pa.pa_decode(q, kc, vc.float(), bt, ctx, 32, 64, 0.125, ws)
+    with pytest.raises(AssertionError, match="columns"):
+        pa.pa_decode(q, kc, vc, bt, ctx, 33, 64, 0.125, ws)        # 33 keys need 3 blocks of 16
+    with pytest.raises(AssertionError, match="columns"):
+        pa.pa_prefill_varlen(q, kc, vc, ctx, ctx, bt, 1, 40, 0.125, q, ws)
+    k_new = torch.zeros((1, 2, 64), dtype=torch.float32)
+    with pytest.raises(AssertionError, match="dtype"):
+        pa.pa_store_kv(k_new, k_new, kc, vc, ctx)
+    with pytest.raises(AssertionError, match="shapes differ"):
+        pa.pa_store_kv(k_new.bfloat16(), k_new.bfloat16(), kc, vc[:2], ctx)

@@ -9,7 +9,7 @@ import torch
 import oracle
 import workloads as W
 from pa_runner import (DEV, HostInputs, assert_close, decode_buffers, default_partition,
-                       run_decode, run_store, sample_seqs, to_f64)
+                       run_decode, run_store, sample_seqs, timed_partition, to_f64)
 
 import paged_kv_cache_114_amd as pa
 
@@ -36,17 +36,24 @@ def test_decode_small_cases(name, partition):
     _decode_vs_oracle(case, partition or default_partition(case))
 
 
-def test_decode_c2_full_all_sequences():
+@pytest.mark.parametrize("policy", ["timed", "default"])
+def test_decode_c2_full_all_sequences(policy):
+    """Every sequence of the batch-64 workload, at the split size bench.py times
+    (256 tokens) and at the tests' other split policy (128)."""
     case = W.c2_decode()
-    _decode_vs_oracle(case, default_partition(case))
+    p = timed_partition(case) if policy == "timed" else default_partition(case)
+    _decode_vs_oracle(case, p)
 
 
 @pytest.mark.parametrize("name", ["c4", "c5"])
-def test_decode_full_size_sampled(name):
-    """Full-size pools in the launch configuration the benchmark uses; the oracle
-    checks a spread of sequences (longest, shortest, random), all heads."""
+@pytest.mark.parametrize("policy", ["timed", "default"])
+def test_decode_full_size_sampled(name, policy):
+    """Full-size pools at the split size bench.py times (C4: one split of 4096
+    tokens; C5: 512-token splits) and at the tests' other policy; the oracle checks a
+    spread of sequences (longest, shortest, random), all heads."""
     case = W.FULL_CASES[name]()
-    _decode_vs_oracle(case, default_partition(case), seqs=sample_seqs(case, 10, seed=1))
+    p = timed_partition(case) if policy == "timed" else default_partition(case)
+    _decode_vs_oracle(case, p, seqs=sample_seqs(case, 10, seed=1))
 
 
 @pytest.mark.parametrize("hq,hkv,d,dtype,bs", [

@@ -23,15 +23,11 @@ THETA = 1e6         # Qwen3's rope_theta
 
 
 def pair_bound(ref, dtype):
-    """Per-element bound.  bf16: 2e-3 + 1e-2 |ref| (the output's own rounding is
-    at most 2^-9 |ref|).  fp32: 1e-5 (1 + |pair|), with |pair| the length of the
-    rotation pair the element belongs to -- the fp32 angle and norm errors scale
-    with it, not with the element, which can cancel to zero."""
+    """Per-element bound, the one stated for the attention outputs: bf16 2e-3 +
+    1e-2 |ref| (the output's own rounding is at most 2^-9 |ref|); fp32 1e-5."""
     if dtype == "bf16":
         return 2e-3 + 1e-2 * np.abs(ref)
-    half = ref.shape[-1] // 2
-    length = np.hypot(ref[..., :half], ref[..., half:])
-    return 1e-5 * (1.0 + np.concatenate([length, length], axis=-1))
+    return np.full(ref.shape, 1e-5)
 
 
 def check(got, ref, dtype, what):

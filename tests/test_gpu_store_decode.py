@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import workloads as W
-from pa_runner import DEV, HostInputs, assert_close, decode_buffers, default_partition, to_f64
+from pa_runner import (DEV, HostInputs, assert_close, decode_buffers, default_partition,
+                       sample_seqs, timed_partition, to_f64)
 
 import paged_kv_cache_114_amd as pa
 
@@ -82,8 +83,69 @@ def test_store_decode_padding_rows():
     check(case)
 
 
-def test_store_decode_full_c2():
-    check(W.FULL_CASES["c2"]())
+@pytest.mark.parametrize("policy", ["timed", "default"])
+def test_store_decode_full_c2(policy):
+    """The batch-64 step at the split size bench.py times (256 tokens, 4 splits for the
+    longest context) and at the other test policy; all 64 sequences against the oracle."""
+    case = W.FULL_CASES["c2"]()
+    check(case, partition=timed_partition(case) if policy == "timed" else None)
+
+
+def check_on_device(case, partition, oracle_seqs):
+    """check() for pools too large to copy to the host whole: the fused and two-call
+    pools are compared on the device, the stored rows against the new K/V, every
+    other slot against the pool before the step; the oracle checks oracle_seqs."""
+    print(f"store_decode (device pools) case={case.name} B={case.num_seqs} P={partition} "
+          f"seqs={oracle_seqs}", flush=True)
+    vals = W.materialize(case, DEV)
+    host = HostInputs(case, vals, oracle_seqs)
+    out_f, kc_f, vc_f = run(case, vals, True, "bshd", partition)
+    out_s, kc_s, vc_s = run(case, vals, False, "bshd", partition)
+    bits = torch.int16 if case.dtype == "bf16" else torch.int32
+    assert torch.equal(out_f.view(bits), out_s.view(bits)), "fused and two-call outputs differ"
+    slots = torch.from_numpy(case.slot_mapping.astype(np.int64)).to(DEV)
+    live = slots >= 0
+    for got, two, before, new in ((kc_f, kc_s, vals["k_cache"], vals["k_new"]),
+                                  (vc_f, vc_s, vals["v_cache"], vals["v_new"])):
+        assert torch.equal(got.view(bits), two.view(bits)), "fused and two-call pools differ"
+        rows = got.view(-1, case.num_kv_heads, case.head_dim)
+        assert torch.equal(rows[slots[live]].view(bits), new[live].view(bits)), "stored rows"
+        rest = got.clone()
+        rest.view(-1, case.num_kv_heads, case.head_dim)[slots[live]] = \
+            before.view(-1, case.num_kv_heads, case.head_dim)[slots[live]]
+        assert torch.equal(rest.view(bits), before.view(bits)), "a slot outside the step changed"
+        del rest
+    got = to_f64(out_f, case.dtype)
+    assert_close(got[host.seqs], host.decode(), case.dtype, case.name)
+
+
+def test_store_decode_full_c5_timed_partition():
+    """The shared-prefix batch at the split size bench.py times (512 tokens, 16 splits
+    for the longest context): the longest shared-prefix and the longest private
+    sequence plus 8 random ones against the oracle."""
+    case = W.FULL_CASES["c5"]()
+    first = case.block_table[:, 0]
+    shared = {b for b in range(case.num_seqs) if int((first == first[b]).sum()) > 1}
+    assert len(shared) == 192
+    lens = case.context_lens
+    sh = [b for b in range(case.num_seqs) if b in shared]
+    pr = [b for b in range(case.num_seqs) if b not in shared]
+    pick = {max(sh, key=lambda b: lens[b]), max(pr, key=lambda b: lens[b])}
+    pick |= set(sample_seqs(case, 10, seed=3))
+    seqs = sorted(pick)
+    p = timed_partition(case)
+    assert p == 512
+    check_on_device(case, p, seqs)
+
+
+def test_store_decode_full_c4_separate_store_branch():
+    """The 512 x 4096 batch at the split size bench.py times (one split): 4,096
+    (sequence, kv head) waves exceed what the fused launch keeps resident, so the
+    library stores in its own launch first (the branch bench.py's C4 step takes)."""
+    case = W.FULL_CASES["c4"]()
+    p = timed_partition(case)
+    assert p == 4096
+    check_on_device(case, p, sample_seqs(case, 8, seed=4))
 
 
 @pytest.mark.parametrize("hq,hkv,d,dtype,bs", [

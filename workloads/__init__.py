@@ -301,6 +301,13 @@ def mixed_batch(n_decode=48, n_chunks=4, chunk=512, n_fresh=2, seed=1146,
                         notes={"rows": "decode rows (Lq=1), chunked-prefill continuations, fresh prompts"})
 
 
+def balanced_prefill(nseq=8, length=2048, seed=1147, name="prefill_8x2048") -> Case:
+    """A balanced varlen prefill: nseq fresh prompts of one length (Qwen3-0.6B head
+    shapes, block 256); the steady-state case of the tile loop."""
+    return prefill_case(name, seed, lengths=np.full(nseq, length),
+                        cached=np.zeros(nseq, np.int64))
+
+
 FULL_CASES = {
     "c1": c1_tiny_decode,
     "c2": c2_decode,
@@ -308,6 +315,7 @@ FULL_CASES = {
     "c4": c4_heavy_decode,
     "c5": c5_shared_prefix_decode,
     "mixed": mixed_batch,
+    "p8x2048": balanced_prefill,
 }
 
 # Scaled-down twins: same head shapes, block sizes and length laws, several
