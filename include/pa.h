@@ -240,6 +240,37 @@ int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
                     size_t workspace_bytes, int32_t dtype, hipStream_t stream);
 
 /*
+ * pa_store_decode_noalloc -- pa_store_decode followed by pa_decode_reduce, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid it).
+ *
+ * The split workspace is a fixed device array inside the library, 64 MiB on
+ * every GPU it runs on, held until the process ends; nothing is allocated or
+ * freed by this call.  A request whose workspace (the size
+ * pa_decode_workspace_size gives) exceeds 64 MiB returns PA_ERR_WORKSPACE
+ * before anything is launched.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different host
+ * threads without ordering) race and give undefined results; calls ordered on
+ * one stream do not.  The array needs no clearing between calls (each call
+ * writes every split statistic it reads).
+ *
+ * Arguments are those of pa_store_decode without workspace / workspace_bytes,
+ * plus out, out_seq_stride, out_head_stride as for pa_decode_reduce; the
+ * results are bit for bit those of pa_store_decode then pa_decode_reduce.
+ */
+int pa_store_decode_noalloc(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                            int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                            const int32_t* slot_mapping, const void* q, int64_t q_seq_stride,
+                            int64_t q_head_stride, void* k_cache, void* v_cache,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int32_t cache_layout, int32_t max_context_len,
+                            int32_t partition_tokens, float scale, void* out,
+                            int64_t out_seq_stride, int64_t out_head_stride, int32_t dtype,
+                            hipStream_t stream);
+
+/*
  * pa_decode_reduce -- merge the splits written by pa_decode.
  *
  * [Intro §9.5]: with m* = max_s m_s, out = sum_s 2^(m_s - m*) acc_s /

@@ -36,6 +36,7 @@ EXPORTS = (
     "pa_decode_workspace_size",
     "pa_decode",
     "pa_store_decode",
+    "pa_store_decode_noalloc",
     "pa_decode_reduce",
     "pa_prefill_workspace_size",
     "pa_prefill_varlen",
@@ -76,6 +77,10 @@ def _load():
     lib.pa_store_decode.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, i64,
                                     vp, i32, i32, i32, i32, i32, i64, i32, i32, i32, f32, vp, sz,
                                     i32, vp]
+    lib.pa_store_decode_noalloc.restype = ctypes.c_int
+    lib.pa_store_decode_noalloc.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp,
+                                            vp, i64, vp, i32, i32, i32, i32, i32, i64, i32, i32,
+                                            i32, f32, vp, i64, i64, i32, vp]
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp, sz, vp, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp]
     lib.pa_prefill_workspace_size.restype = ctypes.c_int
@@ -235,6 +240,24 @@ def pa_store_decode(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_table
         _ptr(v_cache), _ptr(block_table), block_table.stride(0), _ptr(context_lens), b, hq, hkv,
         d, bs, nb, lay, max_context_len, partition_tokens, scale, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_store_decode_noalloc(k_new, v_new, slot_mapping, q, k_cache, v_cache, block_table,
+                            context_lens, max_context_len, partition_tokens, scale, out,
+                            stream=None, layout="bshd") -> None:
+    """pa_store_decode then pa_decode_reduce into ``out [B, Hq, d]``, with the split
+    workspace in the library's own fixed device array (nothing is allocated)."""
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    _check_pool(k_cache, v_cache, q, k_new, v_new, out)
+    _check_table(block_table, bs, max_context_len)
+    b, hq, _ = q.shape
+    assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"
+    _check("pa_store_decode_noalloc", library().pa_store_decode_noalloc(
+        _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1), v_new.stride(0),
+        v_new.stride(1), _ptr(slot_mapping), _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), block_table.stride(0), _ptr(context_lens), b, hq, hkv,
+        d, bs, nb, lay, max_context_len, partition_tokens, scale, _ptr(out), out.stride(0),
+        out.stride(1), _dtype_code(k_cache), _stream(stream)))
 
 
 def pa_decode_reduce(workspace, context_lens, num_splits, partition_tokens, out,

@@ -230,6 +230,49 @@ int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
                        stream);
 }
 
+int pa_store_decode_noalloc(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                            int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                            const int32_t* slot_mapping, const void* q, int64_t q_seq_stride,
+                            int64_t q_head_stride, void* k_cache, void* v_cache,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int32_t cache_layout, int32_t max_context_len,
+                            int32_t partition_tokens, float scale, void* out,
+                            int64_t out_seq_stride, int64_t out_head_stride, int32_t dtype,
+                            hipStream_t stream) {
+  // The size check comes first: a request larger than the fixed workspace is
+  // refused before any pointer is looked at or any runtime call is made.
+  size_t need = 0;
+  int32_t splits = 0;
+  if (num_q_heads <= 0 || head_dim <= 0) return PA_ERR_INVALID_ARG;
+  const int st = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                          partition_tokens, &need, &splits);
+  if (st != PA_OK) return st;
+  if (need > pa::kDecodeScratchBytes) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  // the reduce's own output checks, before the store launch can change the caches
+  const int eb = elt_bytes(dtype);
+  if (!out || out_seq_stride < 0 || out_head_stride < 0) return PA_ERR_INVALID_ARG;
+  if (eb == 0 || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int64_t lane_bytes = int64_t{head_dim} / 64 * eb;
+  if ((reinterpret_cast<uintptr_t>(out) % lane_bytes) || (out_seq_stride * eb) % lane_bytes ||
+      (out_head_stride * eb) % lane_bytes)
+    return PA_ERR_UNSUPPORTED;
+  float* ws = nullptr;
+  if (pa::decode_scratch(&ws) != hipSuccess) return PA_ERR_LAUNCH;
+  const int rc = pa_store_decode(k_new, v_new, k_tok_stride, k_head_stride, v_tok_stride,
+                                 v_head_stride, slot_mapping, q, q_seq_stride, q_head_stride,
+                                 k_cache, v_cache, block_table, block_table_stride, context_lens,
+                                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 num_blocks, cache_layout, max_context_len, partition_tokens,
+                                 scale, ws, pa::kDecodeScratchBytes, dtype, stream);
+  if (rc != PA_OK) return rc;
+  return pa_decode_reduce(ws, pa::kDecodeScratchBytes, context_lens, num_seqs, num_q_heads,
+                          head_dim, splits, partition_tokens, out, out_seq_stride, out_head_stride,
+                          dtype, stream);
+}
+
 int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
                      int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t num_splits,
                      int32_t partition_tokens, void* out, int64_t out_seq_stride,

@@ -34,6 +34,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -428,6 +430,31 @@ hipError_t run_reduce(const ReduceArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// The workspace of pa_store_decode_noalloc: a file-scope device array, one copy
+// per GPU.  In host code its name is only a stand-in for the symbol; the device
+// address is asked of the runtime (once per device, with that device current)
+// and only that address is ever passed to a kernel.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* known[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!known[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    known[dev] = static_cast<float*>(p);
+  }
+  *ptr = known[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.bf16) return a.head_dim == 128 ? pick_group<bf16_t, 128>(a, stream)

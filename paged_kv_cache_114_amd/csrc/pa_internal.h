@@ -110,6 +110,12 @@ struct RopeArgs {
 };
 hipError_t launch_norm_rope_store(const RopeArgs& a, hipStream_t stream);
 
+// The fixed device-resident workspace of pa_store_decode_noalloc: each GPU the
+// library runs on holds one copy for the rest of the process.
+constexpr size_t kDecodeScratchBytes = size_t{64} << 20;
+// The current device's copy (its address asked of the runtime once per device).
+hipError_t decode_scratch(float** ptr);
+
 // The prefill work list is built by one workgroup that holds a per-sequence
 // table in LDS, which bounds the batch.
 constexpr int kPrefillPlanMaxSeqs = 4096;

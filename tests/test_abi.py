@@ -304,3 +304,18 @@ def test_binding_checks_cache_shape_dtype_and_table_width():
         pa.pa_store_kv(k_new, k_new, kc, vc, ctx)
     with pytest.raises(AssertionError, match="shapes differ"):
         pa.pa_store_kv(k_new.bfloat16(), k_new.bfloat16(), kc, vc[:2], ctx)
+
+
+def test_no_alloc_decode_refuses_oversized_requests_before_any_launch():
+    """pa_store_decode_noalloc checks its workspace need against the fixed 64 MiB
+    first: an oversized request returns PA_ERR_WORKSPACE with null pointers, so no
+    pointer was read and nothing was launched."""
+    lib = pa.library()
+    rc = lib.pa_store_decode_noalloc(NULL, NULL, 1024, 128, 1024, 128, NULL, NULL, 2048, 128,
+                                     NULL, NULL, NULL, 16, NULL, 512, 16, 8, 128, 256, 10240, 0,
+                                     4096, 64, 0.088, NULL, 2048, 128, BF16, NULL)
+    assert rc == pa.PA_ERR_WORKSPACE          # 512 x 16 x 64 splits x 130 floats = 272 MiB
+    rc = lib.pa_store_decode_noalloc(NULL, NULL, 1024, 128, 1024, 128, NULL, NULL, 2048, 128,
+                                     NULL, NULL, NULL, 16, NULL, 0, 16, 8, 128, 256, 10240, 0,
+                                     4096, 64, 0.088, NULL, 2048, 128, BF16, NULL)
+    assert rc == pa.PA_OK                     # no sequences: nothing to do
