@@ -3,27 +3,30 @@
 
 A step is one pass of the hot path over one batch of synthetic input: for a
 decode workload, pa_store_decode (this step's K/V rows stored, and the split-K
-partition pass, in one launch) -> pa_decode_reduce; for the prefill workload,
-pa_store_prefill_varlen (the work-list launch, then the tile kernel, which
-reads this step's keys from k/v and stores them).  The two-call steps (pa_store_kv, then pa_decode -> pa_decode_reduce
-or pa_prefill_varlen) are reported beside them.  Inputs are resident in HBM before timing starts.  Before
-every step a 1 GiB buffer is read (outside the timed events) so the 256 MB
-Infinity Cache and the L2s hold no KV: a real engine touches 28 layers'
-caches between two visits to one layer.  The flush only reads, so it leaves
-no dirty lines whose write-back would steal bandwidth from the timed step.
+partition pass, in one launch -- or the store in a launch of its own when the
+batch's grid is larger than the fused kernel keeps resident) -> pa_decode_reduce;
+for a prefill workload, pa_store_prefill_varlen (the work-list launch, then the
+tile kernel, which reads this step's keys from k/v and stores them).  Inputs are
+resident in HBM before timing starts.  Before every step a 1 GiB buffer is read
+(outside the timed events) so the 256 MB Infinity Cache and the L2s hold no KV: a
+real engine touches 28 layers' caches between two visits to one layer.  The flush
+only reads, so it leaves no dirty lines whose write-back would steal bandwidth from
+the timed step.
 
-Default workload: the Qwen3-0.6B one-layer decode (batch 64, contexts uniform
-in [128, 1024], block 256, bf16).  `value` is its KV read rate: the K and V
-bytes the step must read (sum of context lengths x 8 kv heads x 128 x 2 x 2
-bytes) over the measured step time.  The JSON line also carries the roofline
-of the dominant kernel (decode partition pass), the oracle's CPU rate on a
-bounded sample, and (under "also") the heavy decode, the shared-prefix decode,
-the varlen prefill and the mixed chunked-prefill workloads measured the same
-way, the q/k norm + rope + store step over three workloads' new tokens, and
-28-layer decode steps replayed as HIP graphs.
+Default workload: the heavy one-layer decode (batch 512, every context 4096, block
+256, bf16: 8.59 GB of K/V), the largest single-GPU configuration of the metric.
+`value` is its KV read rate: the K and V bytes the step must read (sum of context
+lengths x 8 kv heads x 128 x 2 x 2 bytes) over the measured step time.  The line
+carries the roofline of the dominant kernel (the decode partition pass) and the
+oracle's CPU rate on a bounded sample; under "prefill", the metric's other half:
+the Qwen3-0.6B varlen prefill's TFLOP/s with its own MFMA roofline and oracle
+baseline; under "also", the batch-64 decode, the shared-prefix decode, the mixed
+chunked-prefill step, two-call and layout variants, the q/k norm + rope + store
+step, and 28-layer decode steps replayed as HIP graphs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c5|mixed]
-                       [--no-also | --only KEY,...] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload c4|c2|c3|c5|mixed|p8x2048]
+                       [--no-also | --only KEY,...] [--no-cpu-baseline] [--no-prefill-line]
 """
 
 from __future__ import annotations
@@ -233,7 +236,42 @@ class Runner:
                     step_ms_with_inner_events=sum(split_ms) / steps,
                     wall_ms_per_step=1e3 * wall / steps)
 
-    def main_kernel_amortized(self, layers=16, reps=5):
+    def store_fused_in_launch(self):
+        """Whether pa_store_decode stores inside the partition launch for this batch:
+        the library does unless the grid ((sequence, kv head, split) waves) is larger
+        than what the fused kernel keeps resident while the plain one would keep it
+        all (3 and 4 waves per SIMD on a 256-CU GPU)."""
+        c = self.case
+        waves = c.num_seqs * c.num_kv_heads * self.splits
+        return not (3 * 4 * 256 < waves <= 4 * 4 * 256)
+
+    def partition_events_ms(self, fused=False, reps=10):
+        """Average duration of the partition pass alone: HIP events around it in each
+        of ``reps`` steps, each after a cache flush (the store, when separate, runs
+        before the first event)."""
+        torch, pa, v, c = self.torch, self.pa, self.vals, self.case
+        ev = HipEvents(2 * reps)
+        for r in range(reps):
+            self.flush()
+            if not fused:
+                pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"],
+                               v["slot_mapping"], layout=self.layout)
+            ev.record(2 * r)
+            if fused:
+                pa.pa_store_decode(v["k_new"], v["v_new"], v["slot_mapping"], v["q"],
+                                   v["k_cache"], v["v_cache"], v["block_table"], v["context_lens"],
+                                   c.max_context_len, self.partition, c.scale, self.ws,
+                                   layout=self.layout)
+            else:
+                pa.pa_decode(v["q"], v["k_cache"], v["v_cache"], v["block_table"],
+                             v["context_lens"], c.max_context_len, self.partition, c.scale,
+                             self.ws, layout=self.layout)
+            ev.record(2 * r + 1)
+        torch.cuda.synchronize()
+        ms = sorted(ev.ms(2 * r, 2 * r + 1) for r in range(reps))
+        return ms[len(ms) // 2]
+
+    def main_kernel_amortized(self, layers=16, reps=5, fused=None):
         """Average duration of the step's main launch (the fused store + partition
         pass, or the prefill), from HIP events around ``layers`` back-to-back
         launches, each on its own copy of the pool (cold, as in a model's layer
@@ -246,7 +284,7 @@ class Runner:
             self.flush()
             ev.record(2 * r)
             for kc, vc in pools:
-                if self.kind == "decode" and self.fused_store:
+                if self.kind == "decode" and (self.fused_store if fused is None else fused):
                     pa.pa_store_decode(v["k_new"], v["v_new"], v["slot_mapping"], v["q"], kc, vc,
                                        v["block_table"], v["context_lens"], c.max_context_len,
                                        self.partition, c.scale, self.ws, layout=self.layout)
@@ -324,7 +362,7 @@ def measured_traffic(workload, kernel):
     if not os.path.exists(path):
         return None
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    for f in KERNEL_SOURCES[kernel.removesuffix("_plain").removesuffix("_store")]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     digest = h.hexdigest()[:16]
@@ -364,8 +402,9 @@ def _oracle_task(seqs):
     used = sorted({int(p) for b in seqs
                    for p in d["block_table"][b, :-(-int(d["context_lens"][b]) // bs)]})
     remap = {p: i for i, p in enumerate(used)}
-    kc = d["k_cache"][used]
-    vc = d["v_cache"][used]
+    packed = d["g2p"][used]  # the shared pools hold only the sampled sequences' blocks
+    kc = d["k_cache"][packed]
+    vc = d["v_cache"][packed]
     bt = np.full((len(seqs), d["block_table"].shape[1]), -1, np.int32)
     for r, b in enumerate(seqs):
         n = -(-int(d["context_lens"][b]) // bs)
@@ -393,6 +432,7 @@ def cpu_baseline(name, budget_s=12.0, all_cores_s=8.0):
     over the workload's sequences (in a fixed random order, passing over them again
     while time is left) until about budget_s seconds of oracle time."""
     import numpy as np
+    import torch
     from threadpoolctl import threadpool_limits
 
     import workloads as W
@@ -446,15 +486,29 @@ def cpu_baseline(name, budget_s=12.0, all_cores_s=8.0):
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         per_task = elapsed / max(1, -(-len(done) // 4))
         n_tasks = int(min(40000, max(workers, all_cores_s * workers / max(per_task, 1e-4))))
-        chunks = [[perm[(4 * t + i) % len(perm)] for i in range(4)] for t in range(n_tasks)]
-        kraw = W.raw_numpy(vals["k_cache"], c.dtype)
+        # the workers cycle over the sequences whose blocks fit 2 GiB of shared memory
+        bs = c.block_size
+        block_bytes = 2 * c.block_size * c.num_kv_heads * c.head_dim * c.elt_bytes
+        subset, blocks = [], set()
+        for b in perm:
+            mine = set(int(x) for x in c.block_table[b, :-(-int(c.context_lens[b]) // bs)])
+            if subset and len(blocks | mine) * block_bytes > (2 << 30):
+                break
+            subset.append(b)
+            blocks |= mine
+        used_g = sorted(blocks)
+        g2p = np.full(c.num_blocks, -1, np.int64)
+        g2p[used_g] = np.arange(len(used_g))
+        chunks = [[subset[(4 * t + i) % len(subset)] for i in range(4)] for t in range(n_tasks)]
+        idx = torch.tensor(used_g, dtype=torch.long, device="cuda:0")
+        kraw = W.raw_numpy(vals["k_cache"].index_select(0, idx), c.dtype)
         shm = shared_memory.SharedMemory(create=True, size=2 * kraw.nbytes)
         try:
             pools = np.ndarray((2,) + kraw.shape, dtype=kraw.dtype, buffer=shm.buf)
             pools[0] = kraw
-            pools[1] = W.raw_numpy(vals["v_cache"], c.dtype)
+            pools[1] = W.raw_numpy(vals["v_cache"].index_select(0, idx), c.dtype)
             del kraw
-            meta = {"block_size": c.block_size, "block_table": c.block_table,
+            meta = {"block_size": c.block_size, "block_table": c.block_table, "g2p": g2p,
                     "context_lens": c.context_lens, "num_cached": c.num_cached,
                     "new_seq": c.new_seq, "slot_mapping": c.slot_mapping,
                     "k_new": W.raw_numpy(vals["k_new"], c.dtype),
@@ -485,14 +539,73 @@ def cpu_baseline(name, budget_s=12.0, all_cores_s=8.0):
             v_all = 4 * c.head_dim * c.num_q_heads * pairs / wall / 1e12
         all_cores = {"value": round(v_all, 4), "unit": unit, "cores": workers,
                      "sample": f"{len(seqs_done)} sequence evaluations in {len(chunks)} tasks of "
-                               f"4 sequences on {workers} worker processes (1 BLAS thread each, "
-                               f"pools shared read-only)",
+                               f"4 sequences (cycling over {len(subset)} of the "
+                               f"{c.num_seqs} sequences) on {workers} worker processes (1 BLAS "
+                               f"thread each, their blocks shared read-only)",
                      "seconds": round(wall, 2)}
     return {"value": round(value, 4), "unit": unit, "cores": 1, "kind": "oracle",
             "sample": f"{len(done)} sequence evaluations over {passes} pass(es) of the "
                       f"{c.num_seqs} sequences of {c.name} (store + attention, fp64 NumPy, "
                       f"1 BLAS thread), {elapsed:.1f} s of oracle time",
             "cpu": cpu, "seconds": round(elapsed, 2), "all_cores": all_cores}
+
+
+def main_is_decode(name):
+    import workloads as W
+    return W.FULL_CASES[name]().kind == "decode"
+
+
+def roofline(run, t, name):
+    """The step's rate (``value``) and the roofline block of its dominant kernel.
+
+    Decode: the partition pass (HBM-bound); its launch duration comes from HIP
+    events around 16 back-to-back launches on 16 pool copies after a cache flush
+    when 16 copies fit in 24 GiB, else from events around the pass in each step
+    (C4: 1.4 ms a launch, so the events' few microseconds do not matter).  When the
+    library stores this step's rows in their own launch (a grid larger than the
+    fused kernel keeps resident, as for 512 sequences), the pass timed is the
+    plain partition kernel and its bytes are the KV read only.
+    Prefill: the pa_prefill_varlen call, i.e. the work-list kernel and the tile
+    kernel (MFMA-bound), timed the same way."""
+    pool_bytes = 2 * run.vals["k_cache"].numel() * run.vals["k_cache"].element_size()
+    amortize = pool_bytes * 16 < (24 << 30)
+    traffic_note = ("HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                    "profile of the same kernel source (profiles/hbm_traffic.json); null when the "
+                    "source changed since")
+    if run.kind == "decode":
+        fused_launch = run.fused_store and run.store_fused_in_launch()
+        if amortize:
+            kernel_ms = run.main_kernel_amortized(fused=fused_launch)
+            timing = ("HIP events around 16 back-to-back launches on 16 pool copies after a "
+                      "cache flush, divided by 16")
+        else:
+            kernel_ms = run.partition_events_ms(fused=fused_launch)
+            timing = "HIP events around the partition pass in each step (after a cache flush)"
+        value = run.kv_bytes() / (t["step_ms"] * 1e-3) / 1e9
+        alg = run.kv_bytes() + (run.store_bytes() if fused_launch else 0)
+        achieved = alg / (kernel_ms * 1e-3) / 1e9
+        kname = "decode_partition_kernel"
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(name, kname + ("" if fused_launch else "_plain")),
+                "traffic_source": traffic_note,
+                "algorithmic_bytes": alg,
+                "kernel": kname + (" (with the fused store)" if fused_launch else
+                                   " (plain; this step stores its rows in a launch of its own)"),
+                "kernel_ms": round(kernel_ms, 5), "kernel_ms_timing": timing}
+        return value, "GB/s", roof
+    kernel_ms = run.main_kernel_amortized()
+    value = run.prefill_flops() / (t["step_ms"] * 1e-3) / 1e12
+    achieved = run.prefill_flops() / (kernel_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(name, "prefill_kernel"), "traffic_source": traffic_note,
+            "algorithmic_flops": run.prefill_flops(),
+            "kernel": "pa_prefill_varlen: prefill_plan_kernel + prefill_kernel (tile kernel)",
+            "kernel_ms": round(kernel_ms, 5),
+            "kernel_ms_timing": ("HIP events around 16 back-to-back calls on 16 pool copies "
+                                 "after a cache flush, divided by 16")}
+    return value, "TFLOP/s", roof
 
 
 def graph_decode(name="c2", layers=28, steps=20, warmup=3, partition=None, batch=None,
@@ -612,7 +725,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="c4", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--partition", type=int, default=None,
                     help="decode split size in tokens (default: chosen from the workload)")
     ap.add_argument("--split-keys", type=int, default=None,
@@ -622,6 +735,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="comma-separated keys of the 'also' entries to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill-line", action="store_true",
+                    help="skip the C3 prefill roofline and oracle block of a decode headline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run plain device copies of this size (a known-traffic kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -651,50 +766,27 @@ def main():
     t = main_run.run(args.steps, args.warmup)
     summ = main_run.summary(t)
     c = main_run.case
-    # the dominant kernel's launch duration for the roofline: amortised over 16
-    # cold launches when 16 pool copies fit comfortably, else the per-step events
-    pool_bytes = 2 * main_run.vals["k_cache"].numel() * main_run.vals["k_cache"].element_size()
-    if pool_bytes * 16 < (24 << 30):
-        kernel_ms = main_run.main_kernel_amortized()
-        kernel_timing = ("HIP events around 16 back-to-back launches on 16 pool copies after a "
-                         "cache flush, divided by 16")
-    else:
-        kernel_ms = t["main_ms"]
-        kernel_timing = "HIP events around the launch in each step"
-    if main_run.kind == "decode":
-        value = main_run.kv_bytes() / (t["step_ms"] * 1e-3) / 1e9
-        unit = "GB/s"
-        alg = main_run.kv_bytes() + (main_run.store_bytes() if main_run.fused_store else 0)
-        achieved = alg / (kernel_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(args.workload, "decode_partition_kernel"),
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
-                "algorithmic_bytes": alg,
-                "kernel": "decode_partition_kernel" + (" (with the fused store)"
-                                                       if main_run.fused_store else ""),
-                "kernel_ms": round(kernel_ms, 5),
-                "kernel_ms_timing": kernel_timing,
-                "kernel_ms_events_per_step": round(t["main_ms"], 5)}
-    else:
-        value = main_run.prefill_flops() / (t["step_ms"] * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        achieved = main_run.prefill_flops() / (kernel_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(args.workload, "prefill_kernel"),
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)",
-                "algorithmic_flops": main_run.prefill_flops(),
-                "kernel": "prefill_kernel (with its work-list kernel)",
-                "kernel_ms": round(kernel_ms, 5), "kernel_ms_timing": kernel_timing,
-                "kernel_ms_events_per_step": round(t["main_ms"], 5)}
+    value, unit, roof = roofline(main_run, t, args.workload)
     del main_run
     torch.cuda.empty_cache()
+
+    # The metric's second half: the varlen prefill's TFLOP/s against the bf16 MFMA
+    # peak, on the Qwen3-0.6B varlen batch, with the oracle beside it.
+    prefill_line = None
+    if main_is_decode(args.workload) and not args.no_prefill_line:
+        pr = Runner("c3")
+        tp = pr.run(max(5, args.steps // 2), 3)
+        p_value, p_unit, p_roof = roofline(pr, tp, "c3")
+        prefill_line = {"workload": WORKLOAD_TEXT["c3"], "value": round(p_value, 2),
+                        "unit": p_unit, "ms_per_step": round(tp["step_ms"], 5),
+                        "roofline": p_roof, "detail": pr.summary(tp)}
+        del pr
+        torch.cuda.empty_cache()
 
     also = {}
     only = set(args.only.split(",")) if args.only else None
     if not args.no_also:
-        for name in ("c4", "c5", "c3", "mixed"):
+        for name in ("c2", "c4", "c5", "c3", "mixed"):
             if name == args.workload or (only and name not in only):
                 continue
             try:
@@ -734,7 +826,8 @@ def main():
                 torch.cuda.empty_cache()
             except Exception as e:
                 also[f"norm_rope_store_{name}"] = {"error": f"{type(e).__name__}: {e}"}
-        for key, batch, fused in (("c2_graph28", None, False), ("c2_b4_graph28", 4, False),
+        for key, batch, fused in (("c2_graph28", None, False), ("c2_b16_graph28", 16, False),
+                                  ("c2_b4_graph28", 4, False), ("c2_b1_graph28", 1, False),
                                   ("c2_graph28_fused_rope", None, True)):
             if only and key not in only:
                 continue
@@ -761,10 +854,14 @@ def main():
                    "wall_ms_per_step_incl_cache_flush": round(t["wall_ms_per_step"], 4)},
         "roofline": roof,
         "detail": summ,
-        "also": also,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
+    if prefill_line is not None:
+        line["prefill"] = prefill_line
+        if not args.no_cpu_baseline:
+            line["prefill"]["cpu_baseline"] = cpu_baseline("c3", budget_s=8.0, all_cores_s=6.0)
+    line["also"] = also
     print(json.dumps(line), flush=True)
 
 
