@@ -129,7 +129,7 @@ class Runner:
     """Buffers and launches for one workload; times each step with HIP events."""
 
     def __init__(self, name, partition=None, split_keys=None, layout="bshd", case=None,
-                 fused_store=True):
+                 fused_store=True, shared_prefix=False):
         import torch
 
         import paged_kv_cache_114_amd as pa
@@ -140,6 +140,9 @@ class Runner:
         self.vals = W.materialize(self.case, "cuda:0")
         self.layout = layout
         self.fused_store = fused_store
+        # decode through pa_decode_shared_prefix: the splits inside a group's shared
+        # prefix computed once per group by the MFMA pass
+        self.shared_prefix = shared_prefix
         if layout == "bhsd":  # the pool transposed to [NB, Hkv, bs, d]
             for key in ("k_cache", "v_cache"):
                 self.vals[key] = self.vals[key].permute(0, 2, 1, 3).contiguous()
@@ -165,6 +168,25 @@ class Runner:
     def flush(self):
         self.flush_sink.copy_(self.flush_buf.sum())
 
+    def decode_pass(self, kc, vc, fused):
+        """The partition pass of one decode step (with this step's store when
+        ``fused``) on the pool (kc, vc)."""
+        pa, v, c = self.pa, self.vals, self.case
+        if self.shared_prefix:
+            store = dict(k_new=v["k_new"], v_new=v["v_new"], slot_mapping=v["slot_mapping"])
+            pa.pa_decode_shared_prefix(v["q"], kc, vc, v["block_table"], v["context_lens"],
+                                       v["prefix_group"], v["prefix_tokens"],
+                                       min(int(c.prefix_tokens.max()), c.max_context_len),
+                                       c.max_context_len, self.partition, c.scale, self.ws,
+                                       layout=self.layout, **(store if fused else {}))
+        elif fused:
+            pa.pa_store_decode(v["k_new"], v["v_new"], v["slot_mapping"], v["q"], kc, vc,
+                               v["block_table"], v["context_lens"], c.max_context_len,
+                               self.partition, c.scale, self.ws, layout=self.layout)
+        else:
+            pa.pa_decode(v["q"], kc, vc, v["block_table"], v["context_lens"], c.max_context_len,
+                         self.partition, c.scale, self.ws, layout=self.layout)
+
     def step(self, ev, k, inner=True):
         """One step; events 4k and 4k+3 bracket it.  With ``inner``, events 4k+1 and
         4k+2 also split it into store, main kernel and (decode) reduce -- each
@@ -178,17 +200,8 @@ class Runner:
             pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"], v["slot_mapping"],
                            layout=self.layout)
         mark(4 * k + 1)
-        if fused and self.kind == "decode":  # the store and the partition pass in one launch
-            pa.pa_store_decode(v["k_new"], v["v_new"], v["slot_mapping"], v["q"], v["k_cache"],
-                               v["v_cache"], v["block_table"], v["context_lens"],
-                               c.max_context_len, self.partition, c.scale, self.ws,
-                               layout=self.layout)
-            mark(4 * k + 2)
-            pa.pa_decode_reduce(self.ws, v["context_lens"], self.splits, self.partition,
-                                self.out)
-        elif self.kind == "decode":
-            pa.pa_decode(v["q"], v["k_cache"], v["v_cache"], v["block_table"], v["context_lens"],
-                         c.max_context_len, self.partition, c.scale, self.ws, layout=self.layout)
+        if self.kind == "decode":  # fused: the store and the partition pass in one launch
+            self.decode_pass(v["k_cache"], v["v_cache"], fused)
             mark(4 * k + 2)
             pa.pa_decode_reduce(self.ws, v["context_lens"], self.splits, self.partition,
                                 self.out)
@@ -238,12 +251,13 @@ class Runner:
 
     def store_fused_in_launch(self):
         """Whether pa_store_decode stores inside the partition launch for this batch:
-        the library does unless the grid ((sequence, kv head, split) waves) is larger
-        than what the fused kernel keeps resident while the plain one would keep it
-        all (3 and 4 waves per SIMD on a 256-CU GPU)."""
+        the library does only when the grid ((sequence, kv head, split) waves) fits
+        what the fused kernel keeps resident at once (one 8-wave workgroup per CU at
+        these shapes, 2,048 waves on a 256-CU GPU); larger grids store first in a
+        launch of their own and run the plain kernel (two workgroups per CU)."""
         c = self.case
         waves = c.num_seqs * c.num_kv_heads * self.splits
-        return not (3 * 4 * 256 < waves <= 4 * 4 * 256)
+        return waves <= 8 * 256
 
     def partition_events_ms(self, fused=False, reps=10):
         """Average duration of the partition pass alone: HIP events around it in each
@@ -257,15 +271,7 @@ class Runner:
                 pa.pa_store_kv(v["k_new"], v["v_new"], v["k_cache"], v["v_cache"],
                                v["slot_mapping"], layout=self.layout)
             ev.record(2 * r)
-            if fused:
-                pa.pa_store_decode(v["k_new"], v["v_new"], v["slot_mapping"], v["q"],
-                                   v["k_cache"], v["v_cache"], v["block_table"], v["context_lens"],
-                                   c.max_context_len, self.partition, c.scale, self.ws,
-                                   layout=self.layout)
-            else:
-                pa.pa_decode(v["q"], v["k_cache"], v["v_cache"], v["block_table"],
-                             v["context_lens"], c.max_context_len, self.partition, c.scale,
-                             self.ws, layout=self.layout)
+            self.decode_pass(v["k_cache"], v["v_cache"], fused)
             ev.record(2 * r + 1)
         torch.cuda.synchronize()
         ms = sorted(ev.ms(2 * r, 2 * r + 1) for r in range(reps))
@@ -284,14 +290,8 @@ class Runner:
             self.flush()
             ev.record(2 * r)
             for kc, vc in pools:
-                if self.kind == "decode" and (self.fused_store if fused is None else fused):
-                    pa.pa_store_decode(v["k_new"], v["v_new"], v["slot_mapping"], v["q"], kc, vc,
-                                       v["block_table"], v["context_lens"], c.max_context_len,
-                                       self.partition, c.scale, self.ws, layout=self.layout)
-                elif self.kind == "decode":
-                    pa.pa_decode(v["q"], kc, vc, v["block_table"], v["context_lens"],
-                                 c.max_context_len, self.partition, c.scale, self.ws,
-                                 layout=self.layout)
+                if self.kind == "decode":
+                    self.decode_pass(kc, vc, self.fused_store if fused is None else fused)
                 else:
                     pa.pa_prefill_varlen(v["q"], kc, vc, v["cu_seqlens_q"], v["cu_seqlens_k"],
                                          v["block_table"], c.max_seqlen_q, c.max_context_len,
@@ -325,6 +325,7 @@ class Runner:
             rate = logical / (t["step_ms"] * 1e-3) / 1e9
             kern = logical / (t["main_ms"] * 1e-3) / 1e9
             out = {"workload": c.name, "layout": self.layout, "fused_store": self.fused_store,
+                   "shared_prefix_pass": self.shared_prefix,
                    "kv_GBps_step": round(rate, 1),
                    "decode_kernel_GBps": round(kern, 1),
                    "decode_kernel_frac_hbm": round(kern / HBM_PEAK_GBS, 4),
@@ -735,6 +736,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="comma-separated keys of the 'also' entries to run (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode through pa_decode_shared_prefix (the workload's prefix groups)")
     ap.add_argument("--no-prefill-line", action="store_true",
                     help="skip the C3 prefill roofline and oracle block of a decode headline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -762,7 +765,8 @@ def main():
                           "launches": args.steps}), flush=True)
         return
 
-    main_run = Runner(args.workload, args.partition, args.split_keys)
+    main_run = Runner(args.workload, args.partition, args.split_keys,
+                      shared_prefix=args.shared_prefix)
     t = main_run.run(args.steps, args.warmup)
     summ = main_run.summary(t)
     c = main_run.case
@@ -798,6 +802,21 @@ def main():
                 also[name] = {"error": f"{type(e).__name__}: {e}"}
         # the two-call store + decode, the head-major pool, and smaller blocks
         import workloads as W
+        for key in ("c5_shared_prefix",):
+            if only and key not in only:
+                continue
+            try:
+                r = Runner("c5", shared_prefix=True)
+                t5 = r.run(max(5, args.steps // 2), 3)
+                also[key] = r.summary(t5)
+                also[key]["partition_pass_ms_amortized"] = round(r.main_kernel_amortized(), 5)
+                u = r.case.kv_bytes_unique() / (also[key]["partition_pass_ms_amortized"] * 1e-3) / 1e9
+                also[key]["unique_kv_GBps_amortized"] = round(u, 1)
+                also[key]["unique_frac_hbm_amortized"] = round(u / HBM_PEAK_GBS, 4)
+                del r
+                torch.cuda.empty_cache()
+            except Exception as e:
+                also[key] = {"error": f"{type(e).__name__}: {e}"}
         variants = [("c2_two_call", "c2", "bshd", None, False),
                     ("c4_two_call", "c4", "bshd", None, False),
                     ("c3_two_call", "c3", "bshd", None, False),

@@ -240,6 +240,59 @@ int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
                     size_t workspace_bytes, int32_t dtype, hipStream_t stream);
 
 /*
+ * pa_decode_shared_prefix -- the partition pass of pa_decode (or, with this
+ * step's rows, of pa_store_decode) for a batch in which groups of sequences
+ * share the physical blocks of a common prefix: the prefix cache of
+ * [Intro §10.5], whose sequences that begin with the same prompt point their
+ * first block-table entries at the same blocks.
+ *
+ * Sequence b belongs to group prefix_group[b] (-1: none).  Every member of
+ * group g holds the same block ids in the first ceil(T_g / block_size)
+ * entries of its block_table row, where T_g = min(prefix_tokens[g],
+ * max_prefix_tokens).  For a member with L = context_lens[b] positions, its
+ * splits s < min(floor(T_g / partition_tokens), floor((L - 1) /
+ * partition_tokens)) -- the splits wholly inside the shared prefix, never the
+ * one holding its last position -- are computed for all members of the group
+ * together by a bf16 MFMA pass that reads each prefix key once per 32 query
+ * rows (all query heads of a kv head, 32 / G members at a time) instead of once
+ * per sequence; the partition pass skips them and computes every other split
+ * as pa_decode does.  Afterwards the workspace holds the split statistics
+ * pa_decode defines (the prefix splits agree with pa_decode's to fp32
+ * rounding: P enters the MFMA as a bf16 head plus a bf16 remainder); follow
+ * with pa_decode_reduce.
+ *
+ *   k_new, v_new, slot_mapping   this step's store as in pa_store_decode, or
+ *                  all three NULL for none (then the caches are only read).  With
+ *                  the store, a member's new token (position L - 1) must lie past
+ *                  its group's prefix, L > prefix_tokens[g]: the shared blocks are
+ *                  read by every member and are not written in the same call (a
+ *                  step that does write one stores first, with pa_store_kv).
+ *   prefix_group   int32 [num_seqs], each -1 or in [0, num_groups).
+ *   prefix_tokens  int32 [num_groups], the shared length of each group.
+ *   max_prefix_tokens   a bound on prefix_tokens, at most max_context_len
+ *                  (larger values are cut to it); it sizes the launch.
+ * Members are found on the device, so a group may be any subset of the batch;
+ * the pass launches ceil(num_seqs * G / 32) x (num_groups * num_kv_heads) x
+ * (max_prefix_tokens / partition_tokens) workgroups, of which those past a
+ * group's members or prefix return at once, so it suits batches with a few
+ * groups.  With num_groups = 0 (or max_prefix_tokens < partition_tokens) this
+ * is pa_decode / pa_store_decode.  bf16 only (PA_ERR_UNSUPPORTED otherwise);
+ * every other argument and the error behaviour are as for pa_store_decode.
+ */
+int pa_decode_shared_prefix(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                            int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                            const int32_t* slot_mapping, const void* q, int64_t q_seq_stride,
+                            int64_t q_head_stride, void* k_cache, void* v_cache,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            const int32_t* context_lens, const int32_t* prefix_group,
+                            const int32_t* prefix_tokens, int32_t num_groups,
+                            int32_t max_prefix_tokens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int32_t cache_layout, int32_t max_context_len,
+                            int32_t partition_tokens, float scale, void* workspace,
+                            size_t workspace_bytes, int32_t dtype, hipStream_t stream);
+
+/*
  * pa_store_decode_noalloc -- pa_store_decode followed by pa_decode_reduce, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid it).

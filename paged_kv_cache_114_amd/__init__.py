@@ -37,6 +37,7 @@ EXPORTS = (
     "pa_decode",
     "pa_store_decode",
     "pa_store_decode_noalloc",
+    "pa_decode_shared_prefix",
     "pa_decode_reduce",
     "pa_prefill_workspace_size",
     "pa_prefill_varlen",
@@ -81,6 +82,10 @@ def _load():
     lib.pa_store_decode_noalloc.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp,
                                             vp, i64, vp, i32, i32, i32, i32, i32, i64, i32, i32,
                                             i32, f32, vp, i64, i64, i32, vp]
+    lib.pa_decode_shared_prefix.restype = ctypes.c_int
+    lib.pa_decode_shared_prefix.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, i64, vp, vp,
+                                            vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            i32, i64, i32, i32, i32, f32, vp, sz, i32, vp]
     lib.pa_decode_reduce.restype = ctypes.c_int
     lib.pa_decode_reduce.argtypes = [vp, sz, vp, i32, i32, i32, i32, i32, vp, i64, i64, i32, vp]
     lib.pa_prefill_workspace_size.restype = ctypes.c_int
@@ -258,6 +263,35 @@ def pa_store_decode_noalloc(k_new, v_new, slot_mapping, q, k_cache, v_cache, blo
         _ptr(v_cache), _ptr(block_table), block_table.stride(0), _ptr(context_lens), b, hq, hkv,
         d, bs, nb, lay, max_context_len, partition_tokens, scale, _ptr(out), out.stride(0),
         out.stride(1), _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_decode_shared_prefix(q, k_cache, v_cache, block_table, context_lens, prefix_group,
+                            prefix_tokens, max_prefix_tokens, max_context_len, partition_tokens,
+                            scale, workspace, k_new=None, v_new=None, slot_mapping=None,
+                            stream=None, layout="bshd") -> None:
+    """The partition pass for a batch whose groups share prefix blocks: ``prefix_group
+    [B]`` (-1: none) and ``prefix_tokens [num_groups]`` (int32, on the device); the
+    splits inside a group's prefix are computed once for all its members.  With
+    ``k_new, v_new, slot_mapping`` the step's rows are stored as by pa_store_decode."""
+    nb, bs, hkv, d, lay = _cache_shape(k_cache, layout)
+    store = k_new is not None
+    assert store == (v_new is not None) == (slot_mapping is not None), "store all or nothing"
+    _check_pool(k_cache, v_cache, q, *((k_new, v_new) if store else ()))
+    _check_table(block_table, bs, max_context_len)
+    b, hq, _ = q.shape
+    assert prefix_group.dtype == prefix_tokens.dtype == context_lens.dtype, "int32 metadata"
+    assert prefix_group.numel() >= b, "prefix_group needs one entry per sequence"
+    if store:
+        assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"
+    _check("pa_decode_shared_prefix", library().pa_decode_shared_prefix(
+        _ptr(k_new) if store else None, _ptr(v_new) if store else None,
+        k_new.stride(0) if store else 0, k_new.stride(1) if store else 0,
+        v_new.stride(0) if store else 0, v_new.stride(1) if store else 0,
+        _ptr(slot_mapping) if store else None, _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), block_table.stride(0), _ptr(context_lens),
+        _ptr(prefix_group), _ptr(prefix_tokens), prefix_tokens.numel(), max_prefix_tokens, b,
+        hq, hkv, d, bs, nb, lay, max_context_len, partition_tokens, scale, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _dtype_code(k_cache), _stream(stream)))
 
 
 def pa_decode_reduce(workspace, context_lens, num_splits, partition_tokens, out,

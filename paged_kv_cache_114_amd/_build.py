@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
 
-SOURCES = ["pa_api.hip", "pa_store.hip", "pa_rope.hip", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.hip", "pa_store.hip", "pa_rope.hip", "pa_decode.hip", "pa_prefill.hip",
+           "pa_prefix.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

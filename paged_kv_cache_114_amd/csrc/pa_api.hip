@@ -135,6 +135,12 @@ struct NewRows {  // the fused store of pa_store_decode / pa_store_prefill_varle
   const int32_t* slot_mapping;
 };
 
+struct SharedPrefix {  // the groups of pa_decode_shared_prefix (group null: none)
+  const int32_t* group;
+  const int32_t* tokens;
+  int32_t num_groups, max_tokens;
+};
+
 int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
                   const void* k_cache, const void* v_cache, const int32_t* block_table,
                   int64_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
@@ -142,7 +148,7 @@ int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
                   int32_t block_size, int64_t num_blocks, int32_t cache_layout,
                   int32_t max_context_len, int32_t partition_tokens, float scale,
                   void* workspace, size_t workspace_bytes, int32_t dtype, const NewRows& nr,
-                  hipStream_t stream) {
+                  hipStream_t stream, const SharedPrefix& sp = SharedPrefix{}) {
   const int eb = elt_bytes(dtype);
   if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_context_len < 0 || num_blocks <= 0 || block_size <= 0)
@@ -181,13 +187,25 @@ int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
     return PA_ERR_UNSUPPORTED;
   float* ws = static_cast<float*>(workspace);
   const size_t acc_elems = static_cast<size_t>(num_seqs) * num_q_heads * splits * head_dim;
+  const pa::CacheGeom geom = geom_of(cache_layout, num_kv_heads, block_size, head_dim);
+  // The shared-prefix pass runs only when some group can hold a whole split.
+  const bool prefix = sp.group && sp.num_groups > 0 && sp.max_tokens >= partition_tokens;
+  if (prefix) {
+    pa::PrefixArgs pa_args{q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
+                           block_table_stride, context_lens, sp.group, sp.tokens, sp.num_groups,
+                           sp.max_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           block_size, partition_tokens, splits, scale, ws, ws + acc_elems,
+                           geom};
+    const int rc = launched(pa::launch_prefix_splits(pa_args, stream));
+    if (rc != PA_OK) return rc;
+  }
   pa::DecodeArgs a{q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
                    block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
                    head_dim, block_size, max_context_len, partition_tokens, splits, scale, ws,
-                   ws + acc_elems, dtype == PA_DTYPE_BF16,
-                   geom_of(cache_layout, num_kv_heads, block_size, head_dim), nr.k, nr.v,
+                   ws + acc_elems, dtype == PA_DTYPE_BF16, geom, nr.k, nr.v,
                    nr.k_tok_stride, nr.k_head_stride, nr.v_tok_stride, nr.v_head_stride,
-                   nr.slot_mapping};
+                   nr.slot_mapping, prefix ? sp.group : nullptr, prefix ? sp.tokens : nullptr,
+                   prefix ? sp.num_groups : 0, prefix ? sp.max_tokens : 0};
   return launched(pa::launch_decode(a, stream));
 }
 
@@ -228,6 +246,41 @@ int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
                        NewRows{k_new, v_new, k_tok_stride, k_head_stride, v_tok_stride,
                                v_head_stride, slot_mapping},
                        stream);
+}
+
+int pa_decode_shared_prefix(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                            int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
+                            const int32_t* slot_mapping, const void* q, int64_t q_seq_stride,
+                            int64_t q_head_stride, void* k_cache, void* v_cache,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            const int32_t* context_lens, const int32_t* prefix_group,
+                            const int32_t* prefix_tokens, int32_t num_groups,
+                            int32_t max_prefix_tokens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, int32_t cache_layout, int32_t max_context_len,
+                            int32_t partition_tokens, float scale, void* workspace,
+                            size_t workspace_bytes, int32_t dtype, hipStream_t stream) {
+  if (dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;  // the prefix pass is bf16 MFMA
+  if (num_groups < 0 || max_prefix_tokens < 0 || max_prefix_tokens > max_context_len)
+    return PA_ERR_INVALID_ARG;
+  // the store is all or nothing
+  const bool store = k_new || v_new || slot_mapping;
+  if (store && (!k_new || !v_new || !slot_mapping)) return PA_ERR_INVALID_ARG;
+  if (store && num_blocks > 0 && block_size > 0 &&
+      num_blocks > (INT32_MAX / block_size) + int64_t{1})
+    return PA_ERR_UNSUPPORTED;  // int32 slots
+  if (num_groups > 0 && num_seqs > 0 && max_context_len > 0) {
+    if (!prefix_group || !prefix_tokens) return PA_ERR_INVALID_ARG;
+    if (num_kv_heads > 0 && int64_t{num_groups} * num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  }
+  return decode_common(q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, cache_layout, max_context_len,
+                       partition_tokens, scale, workspace, workspace_bytes, dtype,
+                       NewRows{k_new, v_new, k_tok_stride, k_head_stride, v_tok_stride,
+                               v_head_stride, slot_mapping},
+                       stream, SharedPrefix{prefix_group, prefix_tokens, num_groups,
+                                            max_prefix_tokens});
 }
 
 int pa_store_decode_noalloc(const void* k_new, const void* v_new, int64_t k_tok_stride,

@@ -64,7 +64,9 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t block_stride,
     int32_t slot_stride, int64_t head_stride, const T* k_new, const T* v_new, int64_t k_tok_stride,
     int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
-    const int32_t* slot_mapping, T* k_cache_w, T* v_cache_w) {
+    const int32_t* slot_mapping, T* k_cache_w, T* v_cache_w,
+    const int32_t* __restrict__ prefix_group, const int32_t* __restrict__ prefix_tokens,
+    int32_t num_groups, int32_t max_prefix) {
   using S = DecodeShape<T, D, G>;
   constexpr int kE = S::kE, kR = S::kR, kTpl = S::kTpl, kU = S::kU, kTile = S::kTile;
   extern __shared__ int32_t bt_lds[];
@@ -107,10 +109,17 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     k_new_raw = load16(k_new + b * k_tok_stride + g * k_head_stride + col * kE);
     v_new_raw = load16(v_new + b * v_tok_stride + g * v_head_stride + col * kE);
   }
+  // A member of a shared-prefix group leaves the splits inside its prefix (all
+  // but the one holding its last position) to the shared-prefix pass.
+  const int grp = prefix_group ? prefix_group[b] : -1;  // outside [0, num_groups): none
   // A context longer than max_ctx (a caller error) is cut to it, so no split reads
   // past the staged window.
   const int ctx = min(context_lens[b], max_ctx);
   if (t0 >= ctx) return;  // empty split (uniform over the workgroup): nothing written
+  if (static_cast<unsigned>(grp) < static_cast<unsigned>(num_groups) &&
+      split < min(min(prefix_tokens[grp], max_prefix) / partition_tokens,
+                              (ctx - 1) / partition_tokens))
+    return;  // written by the shared-prefix pass (uniform)
   const int t1 = min(t0 + partition_tokens, ctx);
   const int bs_mask = (1 << bs_log2) - 1;
 
@@ -348,7 +357,8 @@ hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
                      a.geom.head, static_cast<const T*>(a.k_new), static_cast<const T*>(a.v_new),
                      a.k_tok_stride, a.k_head_stride, a.v_tok_stride, a.v_head_stride,
                      a.slot_mapping, static_cast<T*>(const_cast<void*>(a.k_cache)),
-                     static_cast<T*>(const_cast<void*>(a.v_cache)));
+                     static_cast<T*>(const_cast<void*>(a.v_cache)), a.prefix_group,
+                     a.prefix_tokens, a.num_prefix_groups, a.max_prefix_tokens);
   return hipGetLastError();
 }
 
@@ -380,17 +390,20 @@ int64_t resident_waves(int threads, size_t lds) {
   return waves;
 }
 
-// The fused store costs the partition kernel registers (fewer waves resident).
-// When the grid fits the GPU at once only without them (a long-context batch
-// such as 512 sequences x 8 kv heads), the store goes first as its own
-// launch and the plain kernel follows; both ways write the same bits.
+// The fused store costs the partition kernel registers (fewer waves resident:
+// at Qwen3's shape one 8-wave workgroup per CU instead of two).  When the grid
+// does not fit the GPU at once with them (a long-context batch such as 512
+// sequences x 8 kv heads, or a grid of many splits that runs in several
+// rounds, where the waves resident set the bytes in flight), the store goes
+// first as its own launch and the plain kernel follows; both ways write the
+// same bits.
 template <typename T, int D, int G, int NW>
 hipError_t run_with_store(const DecodeArgs& a, hipStream_t stream) {
   const int64_t waves = int64_t{a.num_seqs} * a.num_kv_heads * a.num_splits;
   const size_t lds = ((a.partition_tokens / a.block_size) + 2) * sizeof(int32_t);
   const int64_t fused = resident_waves<decode_partition_kernel<T, D, G, NW, true>>(NW * kWave, lds);
   const int64_t plain = resident_waves<decode_partition_kernel<T, D, G, NW, false>>(NW * kWave, lds);
-  if (waves <= fused || waves > plain) return run_partition<T, D, G, NW, true>(a, stream);
+  if (waves <= fused || plain <= fused) return run_partition<T, D, G, NW, true>(a, stream);
   const StoreArgs sa{a.k_new, a.v_new, a.k_tok_stride, a.k_head_stride, a.v_tok_stride,
                      a.v_head_stride, const_cast<void*>(a.k_cache),
                      const_cast<void*>(a.v_cache), a.slot_mapping, a.num_seqs, a.num_kv_heads,

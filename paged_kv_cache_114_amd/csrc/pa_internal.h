@@ -51,8 +51,37 @@ struct DecodeArgs {
   const void* v_new;
   int64_t k_tok_stride, k_head_stride, v_tok_stride, v_head_stride;
   const int32_t* slot_mapping;
+  // Shared prefixes (prefix_group == nullptr: none).  Sequence b of group
+  // prefix_group[b] in [0, num_prefix_groups) skips its splits s <
+  // min(min(prefix_tokens[group], max_prefix_tokens) / partition_tokens,
+  // (context_lens[b] - 1) / partition_tokens): the shared-prefix pass writes them.
+  const int32_t* prefix_group;
+  const int32_t* prefix_tokens;
+  int32_t num_prefix_groups, max_prefix_tokens;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// The shared-prefix pass (bf16): the split statistics of every member's splits
+// inside its group's prefix, in the layout of the partition pass.
+struct PrefixArgs {
+  const void* q;
+  int64_t q_seq_stride, q_head_stride;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  int64_t block_table_stride;
+  const int32_t* context_lens;
+  const int32_t* prefix_group;
+  const int32_t* prefix_tokens;
+  int32_t num_groups, max_prefix_tokens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
+  int32_t partition_tokens, num_splits;
+  float scale;
+  float* ws_acc;
+  float* ws_ml;
+  CacheGeom geom;
+};
+hipError_t launch_prefix_splits(const PrefixArgs& a, hipStream_t stream);
 
 struct ReduceArgs {
   const float* ws_acc;

@@ -319,3 +319,28 @@ def test_no_alloc_decode_refuses_oversized_requests_before_any_launch():
                                      NULL, NULL, NULL, 16, NULL, 0, 16, 8, 128, 256, 10240, 0,
                                      4096, 64, 0.088, NULL, 2048, 128, BF16, NULL)
     assert rc == pa.PA_OK                     # no sequences: nothing to do
+
+
+def test_shared_prefix_decode_argument_checks():
+    """pa_decode_shared_prefix refuses, before any pointer is read or anything is
+    launched: an fp32 pool (the prefix pass is bf16 MFMA), a store given in part, a
+    prefix bound above max_context_len, and groups without their arrays."""
+    lib = pa.library()
+    fake = 0x10000  # aligned non-null stand-in: never dereferenced on these paths
+
+    def call(dtype=BF16, k_new=NULL, v_new=NULL, slots=NULL, group=fake, tokens=fake,
+             num_groups=1, max_prefix=2048, max_ctx=4096, num_seqs=8):
+        return lib.pa_decode_shared_prefix(
+            k_new, v_new, 1024, 128, 1024, 128, slots, fake, 2048, 128, fake, fake, fake, 16,
+            fake, group, tokens, num_groups, max_prefix, num_seqs, 16, 8, 128, 16, 10240, 0,
+            max_ctx, 512, 0.088, fake, 1 << 30, dtype, NULL)
+
+    assert call(dtype=F32) == pa.PA_ERR_UNSUPPORTED
+    assert call(k_new=fake) == pa.PA_ERR_INVALID_ARG            # v_new, slots missing
+    assert call(k_new=fake, v_new=fake) == pa.PA_ERR_INVALID_ARG
+    assert call(max_prefix=8192) == pa.PA_ERR_INVALID_ARG       # above max_context_len
+    assert call(num_groups=-1) == pa.PA_ERR_INVALID_ARG
+    assert call(group=NULL) == pa.PA_ERR_INVALID_ARG
+    assert call(tokens=NULL) == pa.PA_ERR_INVALID_ARG
+    assert call(num_seqs=0) == pa.PA_OK                          # nothing to do
+    assert call(num_groups=0, num_seqs=0, group=NULL, tokens=NULL) == pa.PA_OK

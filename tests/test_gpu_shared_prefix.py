@@ -1,0 +1,246 @@
+"""pa_decode_shared_prefix: the splits inside a shared prefix computed once per group by
+the MFMA pass, every other split by the partition pass.
+
+Checked against the oracle element by element (the output is the same attention as
+pa_decode's), against pa_store_decode (the splits the partition pass computes are the
+same bits; the pool is stored the same way), and the prefix splits' statistics against
+the oracle's split statistics."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from pa_runner import (DEV, HostInputs, assert_close, decode_buffers, run_store, sample_seqs,
+                       timed_partition, to_f64)
+
+import paged_kv_cache_114_amd as pa
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def max_prefix(case):
+    return min(int(case.prefix_tokens.max()), case.max_context_len) if len(case.prefix_tokens) \
+        else 0
+
+
+def n_skip(case, b, partition, bound):
+    """Prefix splits of sequence b that the MFMA pass writes (the documented rule)."""
+    g = int(case.prefix_group[b])
+    ctx = int(case.context_lens[b])
+    if g < 0 or ctx < 1:
+        return 0
+    return min(min(int(case.prefix_tokens[g]), bound) // partition, (ctx - 1) // partition)
+
+
+def run(case, vals, partition, shared, store, bound=None):
+    """One decode step on fresh copies of the pool; returns (out, k, v, ws, splits)."""
+    kc, vc = vals["k_cache"].clone(), vals["v_cache"].clone()
+    ws, out, splits = decode_buffers(case, partition)
+    ws.fill_(float("nan"))
+    new = dict(k_new=vals["k_new"], v_new=vals["v_new"], slot_mapping=vals["slot_mapping"])
+    if not store:
+        pa.pa_store_kv(vals["k_new"], vals["v_new"], kc, vc, vals["slot_mapping"])
+    if shared:
+        bound = max_prefix(case) if bound is None else bound
+        pa.pa_decode_shared_prefix(vals["q"], kc, vc, vals["block_table"], vals["context_lens"],
+                                   vals["prefix_group"], vals["prefix_tokens"], bound,
+                                   case.max_context_len, partition, case.scale, ws,
+                                   **(new if store else {}))
+    elif store:
+        pa.pa_store_decode(vals["k_new"], vals["v_new"], vals["slot_mapping"], vals["q"], kc, vc,
+                           vals["block_table"], vals["context_lens"], case.max_context_len,
+                           partition, case.scale, ws)
+    else:
+        pa.pa_decode(vals["q"], kc, vc, vals["block_table"], vals["context_lens"],
+                     case.max_context_len, partition, case.scale, ws)
+    pa.pa_decode_reduce(ws, vals["context_lens"], splits, partition, out)
+    torch.cuda.synchronize()
+    return out, kc, vc, ws, splits
+
+
+def split_views(case, ws, splits):
+    b_, hq, d = case.num_seqs, case.num_q_heads, case.head_dim
+    n = b_ * hq * splits
+    acc = ws[:n * d].view(b_, hq, splits, d)
+    ml = ws[n * d:n * (d + 2)].view(b_, hq, splits, 2)
+    return acc, ml
+
+
+def check(case, partition, store=True, oracle_seqs=None, bound=None):
+    bound = max_prefix(case) if bound is None else bound
+    print(f"shared_prefix case={case.name} B={case.num_seqs} G={case.num_q_heads // case.num_kv_heads}"
+          f" d={case.head_dim} bs={case.block_size} P={partition} store={store} bound={bound}",
+          flush=True)
+    vals = W.materialize(case, DEV)
+    host = HostInputs(case, vals, oracle_seqs)
+    out_s, kc_s, vc_s, ws_s, splits = run(case, vals, partition, True, store, bound)
+    out_p, kc_p, vc_p, ws_p, _ = run(case, vals, partition, False, store)
+    # the pool: stored exactly as pa_store_decode stores it
+    assert torch.equal(kc_s.view(torch.int16), kc_p.view(torch.int16)), "K pool"
+    assert torch.equal(vc_s.view(torch.int16), vc_p.view(torch.int16)), "V pool"
+    # splits of the partition pass: the same bits; prefix splits: the same statistics
+    acc_s, ml_s = split_views(case, ws_s, splits)
+    acc_p, ml_p = split_views(case, ws_p, splits)
+    n_prefix_rows = 0
+    for b in range(case.num_seqs):
+        ns = n_skip(case, b, partition, bound)
+        active = -(-int(case.context_lens[b]) // partition)
+        n_prefix_rows += ns
+        if active > ns:
+            assert torch.equal(acc_s[b, :, ns:active], acc_p[b, :, ns:active]), f"seq {b} acc"
+            assert torch.equal(ml_s[b, :, ns:active], ml_p[b, :, ns:active]), f"seq {b} ml"
+        if ns:
+            m_s, m_p = ml_s[b, :, :ns, 0], ml_p[b, :, :ns, 0]
+            l_s, l_p = ml_s[b, :, :ns, 1], ml_p[b, :, :ns, 1]
+            assert torch.all((m_s - m_p).abs() <= 1e-4 * (1 + m_p.abs())), f"seq {b} prefix m"
+            assert torch.all((l_s - l_p).abs() <= 1e-4 * l_p), f"seq {b} prefix l"
+            a_s, a_p = acc_s[b, :, :ns], acc_p[b, :, :ns]
+            assert torch.all((a_s - a_p).abs() <= 1e-4 * (a_p.abs() + l_p[..., None])), \
+                f"seq {b} prefix acc"
+    if bound >= partition and len(case.prefix_tokens):
+        assert n_prefix_rows > 0, "the case exercises no prefix split"
+    got = to_f64(out_s, case.dtype)
+    return assert_close(got[host.seqs], host.decode(), case.dtype, case.name)
+
+
+@pytest.mark.parametrize("partition", [64, 128, 256, 512])
+@pytest.mark.parametrize("store", [True, False])
+def test_shared_prefix_small(partition, store):
+    """The scaled C5 (12 sequences, 9 sharing a 512-token prefix, block 16)."""
+    check(W.SMALL_CASES["c5s"](), partition, store)
+
+
+def grouped_case(name, seed, hq=16, hkv=8, d=128, bs=64, exact=False):
+    """Three groups and private sequences in one batch, members interleaved with the
+    rest: a 256-token prefix shared by 40 sequences (more than one workgroup's rows),
+    one of them a token longer than the prefix (with ``exact``, another exactly the
+    prefix long: its newest token then sits in a shared block, so such a step stores
+    first, in a launch of its own); a 640-token prefix shared by 3; a one-block
+    prefix with a single member; a padding row."""
+    rng = np.random.default_rng(seed)
+    spec = ([(256, int(t)) for t in rng.integers(1, 700, size=38)] +
+            [(256, 0 if exact else 2), (256, 1)] +
+            [(640, int(t)) for t in (1, 100, 900)] + [(bs, 5)])
+    private = [int(x) for x in rng.integers(1, 1500, size=9)]
+    order = rng.permutation(len(spec) + len(private))
+    lengths = np.zeros(len(order), np.int64)
+    members = {256: [], 640: [], bs: []}
+    for pos, k in enumerate(order):
+        if k < len(spec):
+            prefix, tail = spec[k]
+            lengths[pos] = prefix + tail
+            members[prefix].append(pos)
+        else:
+            lengths[pos] = private[k - len(spec)]
+    groups = [(256, members[256]), (640, members[640]), (bs, members[bs])]
+    return W.decode_case(name, seed, lengths=lengths, hq=hq, hkv=hkv, d=d, bs=bs, pad_rows=1,
+                         prefix_groups=groups)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 8, 128), (8, 8, 128), (32, 8, 128), (16, 2, 128),
+                                      (16, 8, 64)])
+@pytest.mark.parametrize("partition", [64, 256])
+def test_shared_prefix_groups_and_edges(hq, hkv, d, partition):
+    """Several groups at once, every GQA group size, both head sizes, members whose
+    newest token is the first or second position past the prefix, a padding row."""
+    case = grouped_case(f"grouped_{hq}_{hkv}_{d}", 5300 + hq + d, hq, hkv, d)
+    check(case, partition)
+
+
+@pytest.mark.parametrize("partition", [64, 128])
+def test_shared_prefix_member_ending_at_prefix(partition):
+    """A member whose context ends exactly at the prefix: its last split is the
+    partition pass's, the splits before it the MFMA pass's (the step's rows stored
+    first by pa_store_kv, then the decode without the store)."""
+    case = grouped_case("grouped_exact", 5350, exact=True)
+    check(case, partition, store=False)
+
+
+def test_shared_prefix_bound_cuts_long_prefixes():
+    """max_prefix_tokens below a group's prefix: only splits under the bound are taken
+    from the MFMA pass, the rest of the prefix is read by the partition pass."""
+    case = grouped_case("grouped_bound", 5400)
+    check(case, 128, bound=384)      # cuts the 640-token prefix to 3 splits
+    check(case, 128, bound=0)        # no prefix pass at all
+    check(case, 256, bound=300)      # one split of the 256- and 640-token prefixes
+
+
+def test_shared_prefix_block_larger_than_split():
+    """Blocks of 256 tokens and 64-token splits: a split is part of one block."""
+    case = W.decode_case("shared_bs256", 5500, bs=256,
+                         lengths=[512 + 3, 512 + 200, 600, 512 + 900, 77],
+                         prefix_groups=[(512, [0, 1, 3])])
+    check(case, 64)
+
+
+def test_shared_prefix_statistics_match_oracle():
+    """The MFMA pass alone: (m, l, acc) of every prefix split equals the oracle's split
+    statistics, in the base-2 units of the workspace."""
+    case = W.SMALL_CASES["c5s"]()
+    p = 128
+    vals = W.materialize(case, DEV)
+    host = HostInputs(case, vals)
+    run_store(vals)
+    ws, _, splits = decode_buffers(case, p)
+    ws.fill_(float("nan"))
+    pa.pa_decode_shared_prefix(vals["q"], vals["k_cache"], vals["v_cache"], vals["block_table"],
+                               vals["context_lens"], vals["prefix_group"], vals["prefix_tokens"],
+                               max_prefix(case), case.max_context_len, p, case.scale, ws)
+    torch.cuda.synchronize()
+    acc, ml = (t.cpu().numpy().astype(np.float64) for t in split_views(case, ws, splits))
+    kc, vc = host.stored()
+    hq, g_size = case.num_q_heads, case.num_q_heads // case.num_kv_heads
+    checked = 0
+    for b in range(case.num_seqs):
+        ns = n_skip(case, b, p, max_prefix(case))
+        if ns == 0:
+            continue
+        n = int(case.context_lens[b])
+        keys = oracle.to_f64(oracle.gather(kc, host.block_table[b], n), "bf16")
+        vals_ = oracle.to_f64(oracle.gather(vc, host.block_table[b], n), "bf16")
+        qf = oracle.to_f64(host.q[b], "bf16")
+        for h in range(hq):
+            parts = oracle.split_partials(qf[h], keys[:, h // g_size], vals_[:, h // g_size],
+                                          case.scale, [(s * p, (s + 1) * p) for s in range(ns)])
+            for s, (m, l, a) in enumerate(parts):
+                assert abs(ml[b, h, s, 0] - m * LOG2E) <= 1e-3 + 1e-4 * abs(m * LOG2E)
+                assert abs(ml[b, h, s, 1] - l) <= 1e-4 * l + 1e-5
+                assert np.all(np.abs(acc[b, h, s] - a) <= 1e-4 * (np.abs(a) + l) + 1e-5)
+                checked += 1
+    assert checked >= 9 * hq * 4  # 9 members x 4 prefix splits of 128 tokens
+
+
+def test_shared_prefix_without_groups_is_store_decode():
+    """No group (num_groups = 0): the same launches and bits as pa_store_decode."""
+    case = W.SMALL_CASES["c2s"]()
+    p = 128
+    vals = W.materialize(case, DEV)
+    vals["prefix_tokens"] = torch.zeros(0, dtype=torch.int32, device=DEV)
+    vals["prefix_group"] = torch.full((case.num_seqs,), -1, dtype=torch.int32, device=DEV)
+    out_s, kc_s, _, _, _ = run(case, vals, p, True, True, bound=0)
+    out_p, kc_p, _, _, _ = run(case, vals, p, False, True)
+    assert torch.equal(out_s.view(torch.int16), out_p.view(torch.int16))
+    assert torch.equal(kc_s.view(torch.int16), kc_p.view(torch.int16))
+
+
+def test_shared_prefix_full_c5_timed_partition():
+    """Full-size C5 at the split size the benchmark times (512 tokens, 16 splits): the
+    longest shared and longest private sequences and 10 others against the oracle,
+    every sequence against pa_store_decode (prefix splits within 1e-4, the rest the
+    same bits, the pool the same bits)."""
+    case = W.FULL_CASES["c5"]()
+    p = timed_partition(case)
+    assert p == 512
+    shared = [b for b in range(case.num_seqs) if case.prefix_group[b] >= 0]
+    private = [b for b in range(case.num_seqs) if case.prefix_group[b] < 0]
+    assert len(shared) == 192
+    pick = {max(shared, key=lambda b: case.context_lens[b]),
+            max(private, key=lambda b: case.context_lens[b])}
+    pick.update(sample_seqs(case, 10, seed=5))
+    check(case, p, True, sorted(pick))

@@ -66,6 +66,37 @@ def test_config_shapes():
     assert len(shared_rows) >= 192
 
 
+def test_prefix_groups_share_exactly_their_prefix_blocks():
+    """prefix_group / prefix_tokens describe the placement: members of a group hold the
+    same physical ids in their first prefix_tokens / block_size entries, and no block
+    is shared outside a group's prefix."""
+    c5 = W.c5_shared_prefix_decode()
+    assert c5.prefix_tokens.tolist() == [2048]
+    members = np.flatnonzero(c5.prefix_group == 0)
+    assert len(members) == 192 and np.all(c5.prefix_group[c5.prefix_group != 0] == -1)
+    first = c5.block_table[members[0], :128]
+    assert all(np.array_equal(c5.block_table[b, :128], first) for b in members)
+    case = W.decode_case("groups", 77, bs=16, lengths=[100, 40, 300, 64, 64, 90, 5],
+                         prefix_groups=[(32, [0, 2, 4]), (64, [3, 5])])
+    assert case.prefix_group.tolist() == [0, -1, 0, 1, 0, 1, -1]
+    assert case.prefix_tokens.tolist() == [32, 64]
+    owners = {}
+    for b in range(case.num_seqs):
+        n = -(-int(case.context_lens[b]) // case.block_size)
+        for j, blk in enumerate(case.block_table[b, :n].tolist()):
+            owners.setdefault(blk, set()).add((b, j))
+    for blk, uses in owners.items():
+        if len(uses) > 1:  # shared: same column, within one group's prefix
+            seqs = {b for b, _ in uses}
+            cols = {j for _, j in uses}
+            groups = {int(case.prefix_group[b]) for b in seqs}
+            assert len(cols) == 1 and len(groups) == 1 and -1 not in groups
+            g = groups.pop()
+            assert next(iter(cols)) < case.prefix_tokens[g] // case.block_size
+    with pytest.raises(ValueError):
+        W.decode_case("short", 78, bs=16, lengths=[20, 40], prefix_groups=[(32, [0, 1])])
+
+
 def test_materialize_poisons_everything_but_stored_tokens():
     case = W.SMALL_CASES["c5s"]()
     vals = W.materialize(case, "cpu")

@@ -57,6 +57,11 @@ class Case:
     new_pos: np.ndarray          # int32 [T]: logical position of each new token
     shared_blocks: int = 0       # physical blocks shared by several sequences
     notes: dict = field(default_factory=dict)
+    # prefix-cache groups: sequence b shares the first prefix_tokens[g] positions
+    # (whole blocks, the same physical ids) with every sequence of group
+    # g = prefix_group[b]; -1: no group
+    prefix_group: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
+    prefix_tokens: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
 
     @property
     def num_seqs(self) -> int:
@@ -135,26 +140,32 @@ class Case:
         return int(total)
 
 
-def _place_blocks(rng, blocks_per_seq, shared_blocks, shared_seqs, pool=None,
-                  pool_factor=1.25):
+def _place_blocks(rng, blocks_per_seq, groups, pool=None, pool_factor=1.25):
     """Random physical placement: returns (block_table, pool size).
 
-    The pool holds ``pool`` blocks (default: 1.25x the blocks needed, rounded
-    up); a random permutation of its ids is dealt out in sequence order."""
-    needed = shared_blocks + int(sum(blocks_per_seq))
+    ``groups`` lists (shared block count, member sequences).  The pool holds
+    ``pool`` blocks (default: 1.25x the blocks needed, rounded up); a random
+    permutation of its ids is dealt out: each group's shared blocks first, then
+    every sequence's own blocks in sequence order, a member's row starting with
+    its group's shared blocks."""
+    needed = sum(n for n, _ in groups) + int(sum(blocks_per_seq))
     if pool is None:
         pool = max(1, math.ceil(pool_factor * needed))
     assert pool >= needed
     perm = rng.permutation(pool).astype(np.int32)
-    shared = perm[:shared_blocks]
-    cursor = shared_blocks
+    cursor = 0
+    front = {}
+    for n, members in groups:
+        for b in members:
+            assert b not in front, "a sequence belongs to one group at most"
+            front[b] = perm[cursor:cursor + n]
+        cursor += n
     nseq = len(blocks_per_seq)
-    shared_seqs = set(shared_seqs)
     rows = []
     for b in range(nseq):
         own = perm[cursor:cursor + blocks_per_seq[b]]
         cursor += blocks_per_seq[b]
-        rows.append(np.concatenate([shared, own]) if b in shared_seqs else own)
+        rows.append(np.concatenate([front[b], own]) if b in front else own)
     width = max(1, max(len(r) for r in rows))
     table = np.full((nseq, width), -1, dtype=np.int32)
     for b, r in enumerate(rows):
@@ -168,8 +179,11 @@ def _slots(table_row, positions, bs):
 
 
 def _finish(name, kind, dtype, hq, hkv, d, bs, seed, lengths, cached, shared_prefix_tokens=0,
-            shared_seqs=(), pad_rows=0, notes=None, pool=None):
+            shared_seqs=(), pad_rows=0, notes=None, pool=None, prefix_groups=None):
     rng_place = np.random.default_rng([seed, 1])
+    if prefix_groups is None:
+        prefix_groups = [(shared_prefix_tokens, list(shared_seqs))] if shared_prefix_tokens and \
+            len(shared_seqs) else []
     lengths = np.asarray(lengths, dtype=np.int64)
     cached = np.asarray(cached, dtype=np.int64)
     nseq = len(lengths)
@@ -177,12 +191,18 @@ def _finish(name, kind, dtype, hq, hkv, d, bs, seed, lengths, cached, shared_pre
             (kind == "prefill" and np.any(cached >= lengths)):
         raise ValueError(f"{name}: cached positions must lie in [0, length) (prefill) or "
                          f"[0, length] (decode)")
-    shared_blocks = shared_prefix_tokens // bs
+    groups = [(int(tokens) // bs, [int(b) for b in members]) for tokens, members in prefix_groups]
+    prefix_group = np.full(nseq, -1, np.int32)
+    for g, (n, members) in enumerate(groups):
+        for b in members:
+            if n * bs > lengths[b]:
+                raise ValueError(f"{name}: sequence {b} is shorter than its shared prefix")
+            prefix_group[b] = g
     per_seq = []
     for b in range(nseq):
         total = math.ceil(int(lengths[b]) / bs)
-        per_seq.append(total - (shared_blocks if b in set(shared_seqs) else 0))
-    table, pool = _place_blocks(rng_place, per_seq, shared_blocks, shared_seqs, pool)
+        per_seq.append(total - (groups[prefix_group[b]][0] if prefix_group[b] >= 0 else 0))
+    table, pool = _place_blocks(rng_place, per_seq, groups, pool)
     slots, seqs, poss = [], [], []
     for b in range(nseq):
         pos = np.arange(int(cached[b]), int(lengths[b]))
@@ -193,6 +213,7 @@ def _finish(name, kind, dtype, hq, hkv, d, bs, seed, lengths, cached, shared_pre
         table = np.concatenate([table, np.full((pad_rows, table.shape[1]), -1, np.int32)])
         lengths = np.concatenate([lengths, np.zeros(pad_rows, np.int64)])
         cached = np.concatenate([cached, np.zeros(pad_rows, np.int64)])
+        prefix_group = np.concatenate([prefix_group, np.full(pad_rows, -1, np.int32)])
         slots.append(np.full(pad_rows, -1, np.int32))
         seqs.append(np.full(pad_rows, -1, np.int32))
         poss.append(np.zeros(pad_rows, np.int32))
@@ -203,17 +224,21 @@ def _finish(name, kind, dtype, hq, hkv, d, bs, seed, lengths, cached, shared_pre
         slot_mapping=np.concatenate(slots).astype(np.int32),
         new_seq=np.concatenate(seqs).astype(np.int32),
         new_pos=np.concatenate(poss).astype(np.int32),
-        shared_blocks=shared_blocks, notes=dict(notes or {}))
+        shared_blocks=sum(n for n, _ in groups), notes=dict(notes or {}),
+        prefix_group=prefix_group,
+        prefix_tokens=np.array([n * bs for n, _ in groups], np.int32))
 
 
 def decode_case(name, seed, *, lengths, hq=16, hkv=8, d=128, dtype="bf16", bs=256,
                 shared_prefix_tokens=0, shared_seqs=(), pad_rows=0, notes=None,
-                pool=None) -> Case:
-    """A decode step: each sequence stores its newest token (position L-1), then reads L keys."""
+                pool=None, prefix_groups=None) -> Case:
+    """A decode step: each sequence stores its newest token (position L-1), then reads L keys.
+    ``prefix_groups``: (prefix tokens, member sequences) pairs; members share the physical
+    blocks of their group's first prefix tokens (rounded down to whole blocks)."""
     lengths = np.asarray(lengths, dtype=np.int64)
     cached = np.maximum(lengths - 1, 0)
     return _finish(name, "decode", dtype, hq, hkv, d, bs, seed, lengths, cached,
-                   shared_prefix_tokens, shared_seqs, pad_rows, notes, pool)
+                   shared_prefix_tokens, shared_seqs, pad_rows, notes, pool, prefix_groups)
 
 
 def prefill_case(name, seed, *, lengths, cached, hq=16, hkv=8, d=128, dtype="bf16",
@@ -393,6 +418,8 @@ def materialize(case: Case, device="cpu", chunk_blocks=None) -> dict:
         "slot_mapping": torch.tensor(case.slot_mapping, **i32),
         "cu_seqlens_q": torch.tensor(case.cu_seqlens_q, **i32),
         "cu_seqlens_k": torch.tensor(case.cu_seqlens_k, **i32),
+        "prefix_group": torch.tensor(case.prefix_group, **i32),
+        "prefix_tokens": torch.tensor(case.prefix_tokens, **i32),
     }
 
 
