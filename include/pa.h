@@ -347,9 +347,12 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
  * take work items -- (sequence, kv head, query tile, key range) -- from a
  * device-built list ordered largest first, so a batch with one long sequence
  * still keeps every compute unit busy.  A query tile whose keys span
- * more than split_keys positions is cut into key ranges of split_keys keys;
+ * more than split_keys positions is cut into ceil(keys / split_keys) key
+ * ranges of equal length (whole 64-key tiles, at most split_keys keys each);
  * the ranges' partial results (the flash-decoding split of [Intro §9.5]
- * applied to prefill) meet in a merge pass.  With S = ceil(max_seqlen_k /
+ * applied to prefill) meet in a merge pass.  A sequence with one query
+ * position (a decode row of a mixed batch) is never cut: its item reads its
+ * keys decode-style, split over the workgroup's waves.  With S = ceil(max_seqlen_k /
  * split_keys) (S = 1 when split_keys is 0, the no-split setting) the
  * workspace holds, in order and 256-byte aligned: the work-list counter
  * (256 bytes), the work list ((ceil(total_q / R) + num_seqs) * S *

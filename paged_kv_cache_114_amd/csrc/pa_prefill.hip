@@ -140,6 +140,196 @@ struct NewKV {
   uint16_t* v_cache;
 };
 
+// A decode row of a mixed batch (a sequence with one query position): taken
+// decode-style instead of as a 64-row MFMA tile with one live row.  The
+// workgroup's waves split the G query heads into groups of at most two and the
+// keys into consecutive ranges; a wave holds its heads' queries and reads every
+// key of its range once, 16 bytes a lane (a head row over kR lanes, 64 / kR
+// keys per load, the loads of the next tile issued before the current one is
+// consumed), with an fp32 online softmax in base 2.  The ranges' (m, l, acc)
+// meet in LDS and the normalised row is written.  With kNew the last key is
+// this step's row, read from the new K/V and written to its slot here.
+// `scratch` (at least kRanges * G * D floats) and `ml_scratch` (kRanges * G * 2
+// floats) are LDS the item does not otherwise use; every thread of the
+// workgroup calls this.
+template <int D, int G, int kWaves, bool kNew>
+__device__ __forceinline__ void decode_row(
+    const uint16_t* __restrict__ q, int64_t q_tok_stride, int64_t q_head_stride,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const int32_t* bt_lds, int bs_log2, int64_t block_stride, int64_t slot_stride,
+    int64_t head_stride, int g, int q_row, int lk, float scale_log2, uint16_t* __restrict__ out,
+    int64_t out_tok_stride, int64_t out_head_stride, const NewKV& nk, float* scratch,
+    float* ml_scratch) {
+  constexpr int kE = 8, kR = D / kE, kTpl = kWave / kR, kU = 2, kTile = kTpl * kU;
+  constexpr int kGW = G < 2 ? G : 2;          // query heads per wave
+  constexpr int kHG = G / kGW;                // head groups
+  constexpr int kRanges = kWaves / kHG;       // key ranges
+  static_assert(kRanges >= 1 && kRanges * kHG == kWaves, "waves must cover heads x ranges");
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int row = lane / kR;
+  const int col = lane % kR;
+  const int hg = wave % kHG;
+  const int range = wave / kHG;
+  const int n_tiles = (lk + kTile - 1) / kTile;
+  const int t0 = (range * n_tiles / kRanges) * kTile;
+  const int t1 = min(((range + 1) * n_tiles / kRanges) * kTile, lk);
+  const int bs_mask = (1 << bs_log2) - 1;
+  const int head0 = g * G + hg * kGW;
+
+  float qf[kGW][kE];
+#pragma unroll
+  for (int i = 0; i < kGW; ++i) {
+    const uint4 raw = load16(q + static_cast<int64_t>(q_row) * q_tok_stride +
+                             static_cast<int64_t>(head0 + i) * q_head_stride + col * kE);
+    Chunk<bf16_t>::widen(raw, qf[i]);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) qf[i][e] *= scale_log2;
+  }
+  // this step's row (kNew): position lk - 1, read from the new K/V
+  uint4 k_new_raw = make_uint4(0, 0, 0, 0), v_new_raw = make_uint4(0, 0, 0, 0);
+  if constexpr (kNew) {
+    k_new_raw = load16(nk.k + static_cast<int64_t>(q_row) * nk.k_tok_b + g * nk.k_head_b +
+                       col * kE * 2);
+    v_new_raw = load16(nk.v + static_cast<int64_t>(q_row) * nk.v_tok_b + g * nk.v_head_b +
+                       col * kE * 2);
+  }
+  const int new_pos = kNew ? lk - 1 : -1;
+
+  float m[kGW], l[kGW], acc[kGW][kE];
+#pragma unroll
+  for (int i = 0; i < kGW; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[i][e] = 0.f;
+  }
+  const uint16_t* kbase = k_cache + g * head_stride + col * kE;
+  const uint16_t* vbase = v_cache + g * head_stride + col * kE;
+  // Keys past t1 read key t1 - 1 (a readable row) and are masked.
+  auto load_tile = [&](int tb, uint4 (&kr)[kU], uint4 (&vr)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = min(tb + u * kTpl + row, t1 - 1);
+      const int64_t off = static_cast<int64_t>(bt_lds[j >> bs_log2]) * block_stride +
+                          (j & bs_mask) * slot_stride;
+      kr[u] = load16(kbase + off);
+      vr[u] = load16(vbase + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto consume = [&](int tb, const uint4 (&kr)[kU], const uint4 (&vr)[kU]) {
+    float sc[kU][kGW];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = tb + u * kTpl + row;
+      float kf[kE];
+      Chunk<bf16_t>::widen(kNew && min(j, t1 - 1) == new_pos ? k_new_raw : kr[u], kf);
+#pragma unroll
+      for (int i = 0; i < kGW; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) d = fmaf(qf[i][e], kf[e], d);
+        d = group_sum<kR>(d);
+        sc[u][i] = j < t1 ? d : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) {
+      float mt = sc[0][i];
+#pragma unroll
+      for (int u = 1; u < kU; ++u) mt = fmaxf(mt, sc[u][i]);
+      mt = across_groups_max<kR>(mt);
+      const float m_new = fmaxf(m[i], mt);  // finite: the first tile starts below t1
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
+      m[i] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        sc[u][i] = __builtin_amdgcn_exp2f(sc[u][i] - m_new);
+        psum += sc[u][i];
+      }
+      l[i] = l[i] * alpha + psum;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[i][e] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = tb + u * kTpl + row;
+      float vf[kE];
+      Chunk<bf16_t>::widen(kNew && min(j, t1 - 1) == new_pos ? v_new_raw : vr[u], vf);
+#pragma unroll
+      for (int i = 0; i < kGW; ++i)
+#pragma unroll
+        for (int e = 0; e < kE; ++e) acc[i][e] = fmaf(sc[u][i], vf[e], acc[i][e]);
+    }
+  };
+  if (t0 < t1) {  // uniform over the wave
+    uint4 ka[kU], va[kU], kb[kU], vb[kU];
+    load_tile(t0, ka, va);
+    int tb = t0;
+    do {
+      load_tile(tb + kTile, kb, vb);
+      consume(tb, ka, va);
+      load_tile(tb + 2 * kTile, ka, va);
+      consume(tb + kTile, kb, vb);
+      tb += 2 * kTile;
+    } while (tb < t1);
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) {
+      l[i] = across_groups_sum<kR>(l[i]);
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[i][e] = across_groups_sum<kR>(acc[i][e]);
+    }
+  }
+  // Partials of (range, head): acc at scratch[(range * G + head) * D], (m, l) at
+  // ml_scratch[(range * G + head) * 2]; an empty range leaves m = -inf, l = 0.
+  if (row == 0) {
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) {
+      float* dst = scratch + (range * G + hg * kGW + i) * D + col * kE;
+#pragma unroll
+      for (int e = 0; e < kE; e += 4)
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) {
+      ml_scratch[(range * G + hg * kGW + i) * 2] = m[i];
+      ml_scratch[(range * G + hg * kGW + i) * 2 + 1] = l[i];
+    }
+  }
+  if constexpr (kNew) {  // this step's row into its slot
+    const int slot = nk.slot_mapping[q_row];
+    if (wave == 0 && row == 0 && slot >= 0) {
+      const int64_t off = static_cast<int64_t>(slot >> bs_log2) * block_stride +
+                          (slot & bs_mask) * slot_stride + g * head_stride + col * kE;
+      *reinterpret_cast<uint4*>(nk.k_cache + off) = k_new_raw;
+      *reinterpret_cast<uint4*>(nk.v_cache + off) = v_new_raw;
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < G * D; t += kWaves * kWave) {
+    const int i = t / D, d = t % D;
+    float m_star = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kRanges; ++r) m_star = fmaxf(m_star, ml_scratch[(r * G + i) * 2]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRanges; ++r) {
+      const float mr = ml_scratch[(r * G + i) * 2];
+      const float c = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr - m_star);
+      lsum = fmaf(c, ml_scratch[(r * G + i) * 2 + 1], lsum);
+      o = fmaf(c, scratch[(r * G + i) * D + d], o);
+    }
+    out[static_cast<int64_t>(q_row) * out_tok_stride +
+        static_cast<int64_t>(g * G + i) * out_head_stride + d] = f32_to_bf16_rne(o / lsum);
+  }
+}
+
 template <int D, int G, bool kNew>
 __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_tok_stride, int64_t q_head_stride,
@@ -251,12 +441,16 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   const int wg_q0 = qt * S::kBM;                            // first query row of the tile
   const int wg_last_pos = ctx0 + min(lq, wg_q0 + S::kBM) - 1;
   const int n_kt = wg_last_pos / kBN + 1;
-  // A tile that needs more than split_tiles key tiles is cut into key ranges
-  // of split_tiles tiles, one item each; their partial results meet in the
-  // merge kernel.  Split 0 always holds key 0, which every row sees.
-  const int n_split = (n_kt + split_tiles - 1) / split_tiles;
-  const int kt_begin = split * split_tiles;
-  const int kt_end = min(n_kt, kt_begin + split_tiles);
+  // A tile that needs more than split_tiles key tiles is cut into
+  // ceil(n_kt / split_tiles) key ranges of equal length (to a tile), one item
+  // each, so the longest range is as short as the count allows; their partial
+  // results meet in the merge kernel.  Split 0 always holds key 0, which every
+  // row sees.  A decode row (lq == 1) is one item over all its keys (see
+  // decode_row).
+  const int n_split = lq == 1 ? 1 : (n_kt + split_tiles - 1) / split_tiles;
+  const int range_tiles = (n_kt + n_split - 1) / n_split;
+  const int kt_begin = split * range_tiles;
+  const int kt_end = min(n_kt, kt_begin + range_tiles);
   const int last_pos = min(kt_end * kBN - 1, wg_last_pos);  // last key this item loads
 
   const int head = g * G + wave / S::kRB;
@@ -311,6 +505,16 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
       }
   }
   __syncthreads();  // bt_lds ready
+
+  if (lq == 1) {  // a decode row: decode-style over all its keys, then the next item
+    if (tid == 0) next_entry = static_cast<int>(gridDim.x + atomicAdd(tickets, 1));
+    static_assert(S::kWaves * 2 * D * 4 <= kBN * D * 2, "decode-row partials fit a tile buffer");
+    decode_row<D, G, S::kWaves, kNew>(
+        q, q_tok_stride, q_head_stride, k_cache, v_cache, bt_lds, bs_log2, block_stride,
+        slot_stride, head_stride, g, q_begin, lk, scale_log2, out, out_tok_stride,
+        out_head_stride, nk, reinterpret_cast<float*>(k_lds0), reinterpret_cast<float*>(v_lds0));
+    continue;  // the loop's barrier keeps the next item's LDS writes behind every read
+  }
 
   // A tile moves from HBM to LDS by DMA (global_load_lds): a wave-wide
   // instruction writes 1 KB of LDS, lane l's 16 bytes at offset 16 l, so each
@@ -662,6 +866,9 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
 // here; tickets[1] the number of entries; tickets[2] the number of split
 // query tiles, listed in merges[] for the merge kernel.
 constexpr int kPlanThreads = 1024;
+// A decode row's item weighs its key tiles divided by this (its waves split the
+// keys and do no MFMA work), for the largest-first order.
+constexpr int kDecodeRowShare = 4;
 constexpr int kPlanBins = 1024;  // weights >= kPlanBins - 1 share the last bin
 
 template <int BM>
@@ -754,9 +961,14 @@ __device__ __forceinline__ void plan_body(
       const int b = lo;
       const int qt = i - tile_start[b];
       const int n_kt = (seq_ctx0[b] + min(seq_lq[b], (qt + 1) * BM) - 1) / kBN + 1;
+      if (seq_lq[b] == 1) {  // a decode row: one item, its keys shared by the waves
+        fn(b, qt, 0, 1, min(max(1, n_kt / kDecodeRowShare), kPlanBins - 1));
+        continue;
+      }
       const int n_split = (n_kt + split_tiles - 1) / split_tiles;
+      const int range_tiles = (n_kt + n_split - 1) / n_split;  // equal lengths, to a tile
       for (int sp = 0; sp < n_split; ++sp)
-        fn(b, qt, sp, n_split, min(min(split_tiles, n_kt - sp * split_tiles), kPlanBins - 1));
+        fn(b, qt, sp, n_split, min(min(range_tiles, n_kt - sp * range_tiles), kPlanBins - 1));
     }
   };
 
