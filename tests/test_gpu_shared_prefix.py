@@ -244,3 +244,52 @@ def test_shared_prefix_full_c5_timed_partition():
             max(private, key=lambda b: case.context_lens[b])}
     pick.update(sample_seqs(case, 10, seed=5))
     check(case, p, True, sorted(pick))
+
+
+def test_shared_prefix_graph_replays_equal_eager():
+    """Captured in a HIP graph, the step (the prefix pass, the partition pass, the
+    reduce) replays the eager result bit for bit, three times with eager work between
+    the replays and once after new queries."""
+    case = W.SMALL_CASES["c5s"]()
+    p = 128
+    vals = W.materialize(case, DEV)
+    run_store(vals)  # the step's rows stored once; the captured step only reads the pool
+    ws, out, splits = decode_buffers(case, p)
+
+    def step():
+        pa.pa_decode_shared_prefix(vals["q"], vals["k_cache"], vals["v_cache"],
+                                   vals["block_table"], vals["context_lens"],
+                                   vals["prefix_group"], vals["prefix_tokens"], max_prefix(case),
+                                   case.max_context_len, p, case.scale, ws)
+        pa.pa_decode_reduce(ws, vals["context_lens"], splits, p, out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    vals["q"].copy_(torch.randn(vals["q"].shape, generator=gen, device=DEV))
+    step()
+    torch.cuda.synchronize()
+    eager2 = out.clone()
+    out.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), eager2.view(torch.int16))
