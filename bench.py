@@ -794,7 +794,8 @@ def main():
             if name == args.workload or (only and name not in only):
                 continue
             try:
-                r = Runner(name)
+                # C5's sequences share prefix blocks: its step declares the groups
+                r = Runner(name, shared_prefix=name == "c5")
                 also[name] = r.summary(r.run(max(5, args.steps // 2), 3))
                 del r
                 torch.cuda.empty_cache()
@@ -802,17 +803,14 @@ def main():
                 also[name] = {"error": f"{type(e).__name__}: {e}"}
         # the two-call store + decode, the head-major pool, and smaller blocks
         import workloads as W
-        for key in ("c5_shared_prefix",):
+        # C5 through pa_store_decode, its prefix groups not declared: every member
+        # reads the shared blocks itself
+        for key in ("c5_prefix_undeclared",):
             if only and key not in only:
                 continue
             try:
-                r = Runner("c5", shared_prefix=True)
-                t5 = r.run(max(5, args.steps // 2), 3)
-                also[key] = r.summary(t5)
-                also[key]["partition_pass_ms_amortized"] = round(r.main_kernel_amortized(), 5)
-                u = r.case.kv_bytes_unique() / (also[key]["partition_pass_ms_amortized"] * 1e-3) / 1e9
-                also[key]["unique_kv_GBps_amortized"] = round(u, 1)
-                also[key]["unique_frac_hbm_amortized"] = round(u / HBM_PEAK_GBS, 4)
+                r = Runner("c5")
+                also[key] = r.summary(r.run(max(5, args.steps // 2), 3))
                 del r
                 torch.cuda.empty_cache()
             except Exception as e:
