@@ -277,7 +277,7 @@ class Runner:
         ms = sorted(ev.ms(2 * r, 2 * r + 1) for r in range(reps))
         return ms[len(ms) // 2]
 
-    def main_kernel_amortized(self, layers=16, reps=5, fused=None):
+    def main_kernel_amortized(self, layers=16, reps=5, fused=None, planned=False):
         """Average duration of the step's main launch (the fused store + partition
         pass, or the prefill), from HIP events around ``layers`` back-to-back
         launches, each on its own copy of the pool (cold, as in a model's layer
@@ -285,6 +285,11 @@ class Runner:
         ``layers`` launches instead of landing on each one."""
         torch, pa, v, c = self.torch, self.pa, self.vals, self.case
         pools = [(v["k_cache"].clone(), v["v_cache"].clone()) for _ in range(layers)]
+        if planned:  # the prefill work list built once for all the layers
+            pa.pa_prefill_plan(v["cu_seqlens_q"], v["cu_seqlens_k"], c.num_new_tokens,
+                               c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_seqlen_q,
+                               c.max_context_len, self.ws, split_keys=self.split_keys)
+        prefill = pa.pa_prefill_varlen_planned if planned else pa.pa_prefill_varlen
         ev = HipEvents(2 * reps)
         for r in range(reps):
             self.flush()
@@ -293,10 +298,9 @@ class Runner:
                 if self.kind == "decode":
                     self.decode_pass(kc, vc, self.fused_store if fused is None else fused)
                 else:
-                    pa.pa_prefill_varlen(v["q"], kc, vc, v["cu_seqlens_q"], v["cu_seqlens_k"],
-                                         v["block_table"], c.max_seqlen_q, c.max_context_len,
-                                         c.scale, self.out, self.ws, split_keys=self.split_keys,
-                                         layout=self.layout)
+                    prefill(v["q"], kc, vc, v["cu_seqlens_q"], v["cu_seqlens_k"],
+                            v["block_table"], c.max_seqlen_q, c.max_context_len, c.scale,
+                            self.out, self.ws, split_keys=self.split_keys, layout=self.layout)
             ev.record(2 * r + 1)
         torch.cuda.synchronize()
         ms = sorted(ev.ms(2 * r, 2 * r + 1) / layers for r in range(reps))
@@ -606,6 +610,13 @@ def roofline(run, t, name):
             "kernel_ms": round(kernel_ms, 5),
             "kernel_ms_timing": ("HIP events around 16 back-to-back calls on 16 pool copies "
                                  "after a cache flush, divided by 16")}
+    # an engine builds the work list once per step for all its layers (pa_prefill_plan)
+    planned_ms = run.main_kernel_amortized(planned=True)
+    roof["planned_call_ms"] = round(planned_ms, 5)
+    roof["planned_call_frac"] = round(run.prefill_flops() / (planned_ms * 1e-3) / 1e12 /
+                                      BF16_MFMA_PEAK_TFLOPS, 4)
+    roof["planned_call_timing"] = ("the same 16 calls through pa_prefill_varlen_planned on one "
+                                   "work list built before them (the layers of one step)")
     return value, "TFLOP/s", roof
 
 

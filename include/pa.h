@@ -456,6 +456,57 @@ int pa_store_prefill_varlen(const void* k_new, const void* v_new, int64_t k_tok_
                             int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
                             hipStream_t stream);
 
+/*
+ * pa_prefill_plan -- build pa_prefill_varlen's work list once for a batch.
+ *
+ * The work list (the (sequence, kv head, query tile, key range) items in
+ * largest-first order) depends only on cu_seqlens_q, cu_seqlens_k, num_seqs,
+ * total_q, the head counts and head_dim, max_seqlen_q, max_seqlen_k and
+ * split_keys -- the attention metadata an engine prepares once per step and
+ * every layer of the step shares [Intro §11.4].  This call writes it into
+ * `workspace` (sized by pa_prefill_workspace_size for the same values);
+ * pa_prefill_varlen_planned and pa_store_prefill_varlen_planned then run a
+ * layer's prefill on it without building it again, for as many calls (layers)
+ * as the step has: each call leaves the list ready for the next (the last of
+ * its workgroups resets the claim counter).  Calls that use one workspace must
+ * be ordered (one stream); the arguments listed above must be the ones the
+ * plan was built with, and a workspace holds one plan at a time (a
+ * pa_prefill_varlen call on it replaces the plan with its own, for the same
+ * metadata an identical one).  Errors as for pa_prefill_varlen.
+ */
+int pa_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                    int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t split_keys,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* pa_prefill_varlen on the work list pa_prefill_plan built in `workspace`
+ * (same arguments; the outputs are bit for bit those of pa_prefill_varlen). */
+int pa_prefill_varlen_planned(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* block_table, int64_t block_table_stride,
+                              int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, int32_t cache_layout, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, float scale, int32_t split_keys,
+                              void* workspace, size_t workspace_bytes, void* out,
+                              int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
+                              hipStream_t stream);
+
+/* pa_store_prefill_varlen on the work list pa_prefill_plan built in
+ * `workspace` (same arguments; outputs and caches bit for bit those of
+ * pa_store_prefill_varlen). */
+int pa_store_prefill_varlen_planned(
+    const void* k_new, const void* v_new, int64_t k_tok_stride, int64_t k_head_stride,
+    int64_t v_tok_stride, int64_t v_head_stride, const int32_t* slot_mapping, const void* q,
+    int64_t q_tok_stride, int64_t q_head_stride, void* k_cache, void* v_cache,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
+    int64_t block_table_stride, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    int32_t cache_layout, int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+    int32_t split_keys, void* workspace, size_t workspace_bytes, void* out,
+    int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

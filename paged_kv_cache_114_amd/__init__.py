@@ -42,6 +42,9 @@ EXPORTS = (
     "pa_prefill_workspace_size",
     "pa_prefill_varlen",
     "pa_store_prefill_varlen",
+    "pa_prefill_plan",
+    "pa_prefill_varlen_planned",
+    "pa_store_prefill_varlen_planned",
 )
 
 
@@ -100,6 +103,12 @@ def _load():
                                             vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i64,
                                             i32, i32, i32, f32, i32, vp, sz, vp, i64, i64, i32,
                                             vp]
+    lib.pa_prefill_plan.restype = ctypes.c_int
+    lib.pa_prefill_plan.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.pa_prefill_varlen_planned.restype = ctypes.c_int
+    lib.pa_prefill_varlen_planned.argtypes = lib.pa_prefill_varlen.argtypes
+    lib.pa_store_prefill_varlen_planned.restype = ctypes.c_int
+    lib.pa_store_prefill_varlen_planned.argtypes = lib.pa_store_prefill_varlen.argtypes
     return lib
 
 
@@ -317,7 +326,7 @@ def pa_prefill_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head
 
 def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
                       max_seqlen_q, max_seqlen_k, scale, out, workspace, split_keys=0,
-                      stream=None, layout="bshd") -> None:
+                      stream=None, layout="bshd", _planned=False) -> None:
     """Causal varlen prefill: ``q, out [Tq, Hq, d]``; K/V read from the paged caches.
     ``workspace``: a device tensor of at least pa_prefill_workspace_size bytes for the
     same sizes and ``split_keys`` (> 0 cuts long query tiles' key loops)."""
@@ -326,7 +335,8 @@ def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tab
     _check_table(block_table, bs, max_seqlen_k)
     tq, hq, _ = q.shape
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("pa_prefill_varlen", library().pa_prefill_varlen(
+    fn = "pa_prefill_varlen_planned" if _planned else "pa_prefill_varlen"
+    _check(fn, getattr(library(), fn)(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
         _ptr(cu_seqlens_k), _ptr(block_table), block_table.stride(0), cu_seqlens_q.shape[0] - 1,
         tq, hq, hkv, d, bs, nb, lay, max_seqlen_q, max_seqlen_k, scale, split_keys,
@@ -336,7 +346,8 @@ def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tab
 
 def pa_store_prefill_varlen(k_new, v_new, slot_mapping, q, k_cache, v_cache, cu_seqlens_q,
                             cu_seqlens_k, block_table, max_seqlen_q, max_seqlen_k, scale, out,
-                            workspace, split_keys=0, stream=None, layout="bshd") -> None:
+                            workspace, split_keys=0, stream=None, layout="bshd",
+                            _planned=False) -> None:
     """Store the query rows' K/V (``[Tq, Hkv, d]``, any token and head strides) through
     ``slot_mapping`` and run the causal varlen prefill; the tile kernel reads these rows
     from ``k_new`` / ``v_new`` and writes them to the cache itself."""
@@ -346,10 +357,31 @@ def pa_store_prefill_varlen(k_new, v_new, slot_mapping, q, k_cache, v_cache, cu_
     tq, hq, _ = q.shape
     assert k_new.stride(-1) == 1 and v_new.stride(-1) == 1, "innermost stride must be 1"
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("pa_store_prefill_varlen", library().pa_store_prefill_varlen(
+    fn = "pa_store_prefill_varlen_planned" if _planned else "pa_store_prefill_varlen"
+    _check(fn, getattr(library(), fn)(
         _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1), v_new.stride(0),
         v_new.stride(1), _ptr(slot_mapping), _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache),
         _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(block_table),
         block_table.stride(0), cu_seqlens_q.shape[0] - 1, tq, hq, hkv, d, bs, nb, lay,
         max_seqlen_q, max_seqlen_k, scale, split_keys, _ptr(workspace), ws_bytes, _ptr(out),
         out.stride(0), out.stride(1), _dtype_code(q), _stream(stream)))
+
+
+def pa_prefill_plan(cu_seqlens_q, cu_seqlens_k, total_q, num_q_heads, num_kv_heads, head_dim,
+                    max_seqlen_q, max_seqlen_k, workspace, split_keys=0, stream=None) -> None:
+    """Build the prefill work list for this metadata into ``workspace`` once; the
+    ``*_planned`` calls then reuse it (every layer of a step)."""
+    _check("pa_prefill_plan", library().pa_prefill_plan(
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.shape[0] - 1, total_q, num_q_heads,
+        num_kv_heads, head_dim, max_seqlen_q, max_seqlen_k, split_keys, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pa_prefill_varlen_planned(*args, **kwargs) -> None:
+    """pa_prefill_varlen on the work list pa_prefill_plan built in ``workspace``."""
+    pa_prefill_varlen(*args, _planned=True, **kwargs)
+
+
+def pa_store_prefill_varlen_planned(*args, **kwargs) -> None:
+    """pa_store_prefill_varlen on the work list pa_prefill_plan built in ``workspace``."""
+    pa_store_prefill_varlen(*args, _planned=True, **kwargs)

@@ -411,7 +411,7 @@ int prefill_common(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                    int32_t max_seqlen_q, int32_t max_seqlen_k, float scale, int32_t split_keys,
                    void* workspace, size_t workspace_bytes, void* out, int64_t out_tok_stride,
                    int64_t out_head_stride, int32_t dtype, const NewRows& nr,
-                   hipStream_t stream) {
+                   hipStream_t stream, bool planned = false) {
   const int eb = elt_bytes(dtype);
   if (eb == 0 || !layout_ok(cache_layout)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_blocks <= 0 ||
@@ -480,8 +480,32 @@ int prefill_common(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                     reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.merges_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.acc_off),
                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off),
-                    out, out_tok_stride, out_head_stride, geom, nr.k ? &store : nullptr};
+                    out, out_tok_stride, out_head_stride, geom, nr.k ? &store : nullptr,
+                    planned, false};
   return launched(pa::launch_prefill(a, stream));
+}
+
+// The shape checks pa_prefill_plan shares with the prefill calls (the ones
+// that decide the work list and the workspace); PA_OK or the error.
+int plan_checks(int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t head_dim, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t split_keys,
+                size_t* need, int32_t* splits) {
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return PA_ERR_INVALID_ARG;
+  if (max_seqlen_q > max_seqlen_k) return PA_ERR_INVALID_ARG;
+  if (!group_ok(num_q_heads, num_kv_heads)) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+      return PA_ERR_INVALID_ARG;
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (!head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int st = pa_prefill_workspace_size(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                           max_seqlen_k, split_keys, need, splits);
+  if (st != PA_OK) return st;
+  if (num_seqs > pa::kPrefillPlanMaxSeqs) return PA_ERR_UNSUPPORTED;
+  const int64_t rows = pa::prefill_rows_per_tile(num_q_heads / num_kv_heads);
+  if ((max_seqlen_q + rows - 1) / rows > 65535 || *splits > 32767) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
 }
 
 }  // namespace
@@ -527,6 +551,72 @@ int pa_store_prefill_varlen(const void* k_new, const void* v_new, int64_t k_tok_
                         NewRows{k_new, v_new, k_tok_stride, k_head_stride, v_tok_stride,
                                 v_head_stride, slot_mapping},
                         stream);
+}
+
+int pa_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                    int32_t total_q, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t split_keys,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  int32_t splits = 1;
+  const int st = plan_checks(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, max_seqlen_q,
+                             max_seqlen_k, split_keys, &need, &splits);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
+  if (!cu_seqlens_q || !cu_seqlens_k || !workspace) return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
+  const PrefillLayout lay =
+      prefill_layout(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, splits);
+  pa::PrefillArgs a{nullptr, 0, 0, nullptr, nullptr, cu_seqlens_q, cu_seqlens_k, nullptr, 0,
+                    num_seqs, num_q_heads, num_kv_heads, head_dim, 8, max_seqlen_q, max_seqlen_k,
+                    total_q, 1.f, split_keys, splits, static_cast<uint32_t*>(workspace),
+                    reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.items_off),
+                    reinterpret_cast<int2*>(static_cast<char*>(workspace) + lay.merges_off),
+                    nullptr, nullptr, nullptr, 0, 0, pa::CacheGeom{0, 0, 0}, nullptr, false,
+                    true};
+  return launched(pa::launch_prefill(a, stream));
+}
+
+int pa_prefill_varlen_planned(const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* block_table, int64_t block_table_stride,
+                              int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, int32_t cache_layout, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, float scale, int32_t split_keys,
+                              void* workspace, size_t workspace_bytes, void* out,
+                              int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype,
+                              hipStream_t stream) {
+  return prefill_common(q, q_tok_stride, q_head_stride, k_cache, v_cache, cu_seqlens_q,
+                        cu_seqlens_k, block_table, block_table_stride, num_seqs, total_q,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        cache_layout, max_seqlen_q, max_seqlen_k, scale, split_keys, workspace,
+                        workspace_bytes, out, out_tok_stride, out_head_stride, dtype,
+                        NewRows{nullptr, nullptr, 0, 0, 0, 0, nullptr}, stream, true);
+}
+
+int pa_store_prefill_varlen_planned(
+    const void* k_new, const void* v_new, int64_t k_tok_stride, int64_t k_head_stride,
+    int64_t v_tok_stride, int64_t v_head_stride, const int32_t* slot_mapping, const void* q,
+    int64_t q_tok_stride, int64_t q_head_stride, void* k_cache, void* v_cache,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
+    int64_t block_table_stride, int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    int32_t cache_layout, int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+    int32_t split_keys, void* workspace, size_t workspace_bytes, void* out,
+    int64_t out_tok_stride, int64_t out_head_stride, int32_t dtype, hipStream_t stream) {
+  if (num_seqs > 0 && total_q > 0 && max_seqlen_q > 0 && (!k_new || !v_new || !slot_mapping))
+    return PA_ERR_INVALID_ARG;
+  return prefill_common(q, q_tok_stride, q_head_stride, k_cache, v_cache, cu_seqlens_q,
+                        cu_seqlens_k, block_table, block_table_stride, num_seqs, total_q,
+                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        cache_layout, max_seqlen_q, max_seqlen_k, scale, split_keys, workspace,
+                        workspace_bytes, out, out_tok_stride, out_head_stride, dtype,
+                        NewRows{k_new, v_new, k_tok_stride, k_head_stride, v_tok_stride,
+                                v_head_stride, slot_mapping},
+                        stream, true);
 }
 
 }  // extern "C"

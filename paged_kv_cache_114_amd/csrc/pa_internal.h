@@ -116,6 +116,8 @@ struct PrefillArgs {
   int64_t out_tok_stride, out_head_stride;
   CacheGeom geom;
   const StoreArgs* store;  // non-null: this step's K/V store, in the work-list launch
+  bool planned;            // the work list is in the workspace already: no plan launch
+  bool plan_only;          // only the plan launch (pa_prefill_plan)
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -856,6 +856,13 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     }
   }
   }  // next item
+  // The last workgroup to leave resets the claim counter (every other one has
+  // made its final claim before it counted itself out), so the work list can
+  // serve the next call with the same metadata without being rebuilt.
+  if (tid == 0 && atomicAdd(&tickets[3], 1u) == gridDim.x - 1) {
+    atomicExch(&tickets[0], 0u);
+    atomicExch(&tickets[3], 0u);
+  }
 }
 
 // Work list of the prefill kernel, built on the device by one workgroup: one
@@ -993,6 +1000,7 @@ __device__ __forceinline__ void plan_body(
     tickets[0] = 0u;
     tickets[1] = static_cast<uint32_t>(n_entries);
     tickets[2] = static_cast<uint32_t>(n_merges);
+    tickets[3] = 0u;  // workgroups of the tile kernel that have left
   }
 }
 
@@ -1125,11 +1133,15 @@ hipError_t run(const PrefillArgs& a, const NewKV& nk, hipStream_t stream) {
   const size_t bt_bytes = static_cast<size_t>((a.max_seqlen_k + a.block_size - 1) >> bs_log2) * 4;
   // split_tiles >= every tile's key-tile count when nothing is split
   const int split_tiles = a.num_splits > 1 ? a.split_keys / kBN : (a.max_seqlen_k + kBN - 1) / kBN;
-  hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
-                     a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, a.max_seqlen_k, split_tiles,
-                     a.num_kv_heads, a.tickets, a.items, a.merges);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!a.planned) {  // else the work list is in the workspace already (pa_prefill_plan)
+    hipLaunchKernelGGL((prefill_plan_kernel<S::kBM>), dim3(1), dim3(kPlanThreads), 0, stream,
+                       a.cu_seqlens_q, a.cu_seqlens_k, a.num_seqs, a.max_seqlen_k, split_tiles,
+                       a.num_kv_heads, a.tickets, a.items, a.merges);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.plan_only) return hipSuccess;
   // one workgroup per resident slot: they stay until the work list is empty
   const int slots = resident_slots<D, G, kNew>(bt_bytes, &err);
   if (err != hipSuccess) return err;

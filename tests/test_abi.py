@@ -344,3 +344,23 @@ def test_shared_prefix_decode_argument_checks():
     assert call(tokens=NULL) == pa.PA_ERR_INVALID_ARG
     assert call(num_seqs=0) == pa.PA_OK                          # nothing to do
     assert call(num_groups=0, num_seqs=0, group=NULL, tokens=NULL) == pa.PA_OK
+
+
+def test_prefill_plan_argument_checks():
+    """pa_prefill_plan refuses what the prefill calls refuse, before any launch."""
+    lib = pa.library()
+    fake = 0x10000
+    big = 1 << 30
+    # (cu_q, cu_k, num_seqs, total_q, hq, hkv, d, max_q, max_k, split_keys, ws, ws_bytes)
+    assert lib.pa_prefill_plan(fake, fake, 8, 6000, 16, 8, 128, 2048, 2048, 0, NULL, big,
+                               NULL) == pa.PA_ERR_INVALID_ARG            # no workspace
+    assert lib.pa_prefill_plan(fake, fake, 8, 6000, 16, 8, 128, 2048, 2048, 0, fake, 64,
+                               NULL) == pa.PA_ERR_WORKSPACE              # too small
+    assert lib.pa_prefill_plan(fake, fake, 8, 6000, 16, 8, 96, 2048, 2048, 0, fake, big,
+                               NULL) == pa.PA_ERR_UNSUPPORTED            # head_dim 96
+    assert lib.pa_prefill_plan(fake, fake, 8, 6000, 16, 8, 128, 4096, 2048, 0, fake, big,
+                               NULL) == pa.PA_ERR_INVALID_ARG            # max_q > max_k
+    assert lib.pa_prefill_plan(fake, fake, 8, 6000, 16, 8, 128, 2048, 2048, 100, fake, big,
+                               NULL) == pa.PA_ERR_UNSUPPORTED            # split_keys % 64
+    assert lib.pa_prefill_plan(NULL, NULL, 0, 0, 16, 8, 128, 0, 0, 0, NULL, 0,
+                               NULL) == pa.PA_OK                         # empty batch
