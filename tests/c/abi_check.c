@@ -50,6 +50,21 @@ int main(void) {
                                  NULL, NULL, NULL, NULL, 8, 8, 6000, 16, 8, 128, 256, 64,
                                  PA_CACHE_BSHD, 2048, 2048, 0.088f, 0, NULL, 0, NULL, 2048, 128,
                                  PA_DTYPE_BF16, NULL) == PA_ERR_INVALID_ARG);
+  EXPECT(pa_prefill_plan(NULL, NULL, 0, 0, 16, 8, 128, 0, 0, 0, NULL, 0, NULL) == PA_OK);
+  EXPECT(pa_prefill_plan(NULL, NULL, 8, 6000, 16, 8, 128, 2048, 2048, 0, NULL, 0, NULL) ==
+         PA_ERR_INVALID_ARG);
+  EXPECT(pa_prefill_varlen_planned(NULL, 2048, 128, NULL, NULL, NULL, NULL, NULL, 8, 8, 6000, 16,
+                                   8, 128, 256, 64, PA_CACHE_BSHD, 2048, 2048, 0.088f, 0, NULL,
+                                   0, NULL, 2048, 128, PA_DTYPE_F32, NULL) == PA_ERR_UNSUPPORTED);
+  EXPECT(pa_store_prefill_varlen_planned(NULL, NULL, 1024, 128, 1024, 128, NULL, NULL, 2048, 128,
+                                         NULL, NULL, NULL, NULL, NULL, 8, 8, 6000, 16, 8, 128,
+                                         256, 64, PA_CACHE_BSHD, 2048, 2048, 0.088f, 0, NULL, 0,
+                                         NULL, 2048, 128, PA_DTYPE_BF16,
+                                         NULL) == PA_ERR_INVALID_ARG);
+  EXPECT(pa_decode_shared_prefix(NULL, NULL, 1024, 128, 1024, 128, NULL, NULL, 2048, 128, NULL,
+                                 NULL, NULL, 16, NULL, NULL, NULL, 1, 2048, 8, 16, 8, 128, 16,
+                                 100, PA_CACHE_BSHD, 4096, 512, 0.088f, NULL, 0, PA_DTYPE_F32,
+                                 NULL) == PA_ERR_UNSUPPORTED);
   if (failures == 0) printf("abi_check: all checks passed\n");
   return failures == 0 ? 0 : 1;
 }
