@@ -587,16 +587,26 @@ def roofline(run, t, name):
             kernel_ms = run.partition_events_ms(fused=fused_launch)
             timing = "HIP events around the partition pass in each step (after a cache flush)"
         value = run.kv_bytes() / (t["step_ms"] * 1e-3) / 1e9
-        alg = run.kv_bytes() + (run.store_bytes() if fused_launch else 0)
-        achieved = alg / (kernel_ms * 1e-3) / 1e9
         kname = "decode_partition_kernel"
+        if run.shared_prefix:
+            # the prefix pass reads each group's shared blocks once and the partition
+            # pass the rest: together every K/V byte once (the unique bytes)
+            alg = run.case.kv_bytes_unique() + (run.store_bytes() if fused_launch else 0)
+            traffic = measured_traffic(name + "_shared_prefix",
+                                       kname + ("" if fused_launch else "_plain"))
+            kdesc = ("pa_decode_shared_prefix: prefix_split_kernel + " + kname +
+                     (" (with the fused store)" if fused_launch else
+                      " (plain; this step stores its rows in a launch of its own)"))
+        else:
+            alg = run.kv_bytes() + (run.store_bytes() if fused_launch else 0)
+            traffic = measured_traffic(name, kname + ("" if fused_launch else "_plain"))
+            kdesc = kname + (" (with the fused store)" if fused_launch else
+                             " (plain; this step stores its rows in a launch of its own)")
+        achieved = alg / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(name, kname + ("" if fused_launch else "_plain")),
-                "traffic_source": traffic_note,
-                "algorithmic_bytes": alg,
-                "kernel": kname + (" (with the fused store)" if fused_launch else
-                                   " (plain; this step stores its rows in a launch of its own)"),
+                "traffic": traffic, "traffic_source": traffic_note,
+                "algorithmic_bytes": alg, "kernel": kdesc,
                 "kernel_ms": round(kernel_ms, 5), "kernel_ms_timing": timing}
         return value, "GB/s", roof
     kernel_ms = run.main_kernel_amortized()

@@ -262,11 +262,15 @@ int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
  * with pa_decode_reduce.
  *
  *   k_new, v_new, slot_mapping   this step's store as in pa_store_decode, or
- *                  all three NULL for none (then the caches are only read).  With
- *                  the store, a member's new token (position L - 1) must lie past
- *                  its group's prefix, L > prefix_tokens[g]: the shared blocks are
- *                  read by every member and are not written in the same call (a
- *                  step that does write one stores first, with pa_store_kv).
+ *                  all three NULL for none (then the caches are only read).  The
+ *                  store runs in the prefix pass's launch, alongside its reads of
+ *                  the shared blocks, and the partition pass after it reads the
+ *                  stored rows from the cache; so no stored slot may be one the
+ *                  prefix pass reads: a member's new token (position L - 1) must
+ *                  lie past its group's prefix, L > prefix_tokens[g], and no
+ *                  slot_mapping entry may point at a group's first T_g positions
+ *                  (a step that does write there stores first, with
+ *                  pa_store_kv).
  *   prefix_group   int32 [num_seqs], each -1 or in [0, num_groups).
  *   prefix_tokens  int32 [num_groups], the shared length of each group.
  *   max_prefix_tokens   a bound on prefix_tokens, at most max_context_len

@@ -190,21 +190,30 @@ int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
   const pa::CacheGeom geom = geom_of(cache_layout, num_kv_heads, block_size, head_dim);
   // The shared-prefix pass runs only when some group can hold a whole split.
   const bool prefix = sp.group && sp.num_groups > 0 && sp.max_tokens >= partition_tokens;
+  NewRows rows = nr;
   if (prefix) {
+    // This step's store runs in the prefix pass's launch (its rows lie past every
+    // group's prefix, so it never writes what that pass reads), and the partition
+    // pass after it reads the stored rows from the cache.
+    const pa::StoreArgs store{nr.k, nr.v, nr.k_tok_stride, nr.k_head_stride, nr.v_tok_stride,
+                              nr.v_head_stride, const_cast<void*>(k_cache),
+                              const_cast<void*>(v_cache), nr.slot_mapping, num_seqs,
+                              num_kv_heads, head_dim, block_size, eb, geom};
     pa::PrefixArgs pa_args{q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
                            block_table_stride, context_lens, sp.group, sp.tokens, sp.num_groups,
                            sp.max_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, partition_tokens, splits, scale, ws, ws + acc_elems,
-                           geom};
+                           geom, nr.k ? &store : nullptr};
     const int rc = launched(pa::launch_prefix_splits(pa_args, stream));
     if (rc != PA_OK) return rc;
+    rows = NewRows{nullptr, nullptr, 0, 0, 0, 0, nullptr};
   }
   pa::DecodeArgs a{q, q_seq_stride, q_head_stride, k_cache, v_cache, block_table,
                    block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
                    head_dim, block_size, max_context_len, partition_tokens, splits, scale, ws,
-                   ws + acc_elems, dtype == PA_DTYPE_BF16, geom, nr.k, nr.v,
-                   nr.k_tok_stride, nr.k_head_stride, nr.v_tok_stride, nr.v_head_stride,
-                   nr.slot_mapping, prefix ? sp.group : nullptr, prefix ? sp.tokens : nullptr,
+                   ws + acc_elems, dtype == PA_DTYPE_BF16, geom, rows.k, rows.v,
+                   rows.k_tok_stride, rows.k_head_stride, rows.v_tok_stride, rows.v_head_stride,
+                   rows.slot_mapping, prefix ? sp.group : nullptr, prefix ? sp.tokens : nullptr,
                    prefix ? sp.num_groups : 0, prefix ? sp.max_tokens : 0};
   return launched(pa::launch_decode(a, stream));
 }

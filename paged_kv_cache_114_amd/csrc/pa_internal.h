@@ -80,6 +80,7 @@ struct PrefixArgs {
   float* ws_acc;
   float* ws_ml;
   CacheGeom geom;
+  const StoreArgs* store;  // non-null: this step's K/V store, by extra workgroups of the launch
 };
 hipError_t launch_prefix_splits(const PrefixArgs& a, hipStream_t stream);
 

@@ -639,8 +639,9 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // S^T = K Q^T for one 64-key tile: two 32-key accumulator chains.  The K
   // operand reads run kLead steps ahead of their MFMAs, in an order the
   // scheduler may not change: left to itself it issued each read right before
-  // its MFMA, which then waited the LDS latency (C3 62.2 -> 58.2 us, mixed
-  // batch 66.6 -> 61.5 us; leads of 3 and 4 were no better).
+  // its MFMA, which then waited the LDS latency (8 prompts of 64..2048: 62.2
+  // -> 58.2 us; a chunked-prefill batch with decode rows: 66.6 -> 61.5 us;
+  // leads of 3 and 4 were no better).
   auto qk = [&](const uint16_t* kt_lds, f32x16_t (&acc_s)[2]) {
     acc_s[0] = f32x16_t{};
     acc_s[1] = f32x16_t{};

@@ -38,8 +38,11 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_store_rows.h"
 
 namespace pa {
 namespace {
@@ -90,7 +93,8 @@ __global__ __launch_bounds__(kWavesWg * kWave) void prefix_split_kernel(
     const int32_t* __restrict__ prefix_tokens, int32_t num_seqs, int32_t num_kv_heads,
     int32_t bs_log2, int32_t max_prefix, int32_t partition_tokens, int32_t num_splits,
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    int64_t block_stride, int64_t slot_stride, int64_t head_stride) {
+    int64_t block_stride, int64_t slot_stride, int64_t head_stride, StoreRows store,
+    int32_t store_x) {
   using S = PrefixShape<D>;
   constexpr int kMembers = kRowsWg / G;  // members per workgroup
   __shared__ __attribute__((aligned(1024))) uint16_t region[kWavesWg][S::kRegionElems];
@@ -105,6 +109,14 @@ __global__ __launch_bounds__(kWavesWg * kWave) void prefix_split_kernel(
   const int lane = tid % kWave;
   const int half = lane / 32;
   const int col = lane % 32;
+  // The last store_x columns of the grid copy this step's K/V rows into the
+  // cache instead (none when store.rows is 0); a stored row is never a slot
+  // this pass reads (the new positions lie past every group's prefix).
+  if (static_cast<int>(blockIdx.x) >= static_cast<int>(gridDim.x) - store_x) {
+    const int wg = blockIdx.x - (gridDim.x - store_x) + store_x * (blockIdx.y + gridDim.y * blockIdx.z);
+    store_rows<uint4>(store, wg * kWavesWg + wave, store_x * gridDim.y * gridDim.z * kWavesWg);
+    return;
+  }
   const int tile = blockIdx.x;
   const int grp = blockIdx.y / num_kv_heads;
   const int h = blockIdx.y % num_kv_heads;
@@ -354,7 +366,17 @@ hipError_t run_prefix(const PrefixArgs& a, hipStream_t stream) {
   const int bs_log2 = __builtin_ctz(static_cast<unsigned>(a.block_size));
   const size_t lds = (static_cast<size_t>(a.partition_tokens / a.block_size) + 2) * sizeof(int32_t);
   const int tiles = (a.num_seqs * G + kRowsWg - 1) / kRowsWg;
-  dim3 grid(tiles, a.num_groups * a.num_kv_heads, a.max_prefix_tokens / a.partition_tokens);
+  StoreRows store{};  // rows = 0: no store
+  int store_x = 0;
+  if (a.store) {
+    if (!store_rows_16(*a.store, &store)) return hipErrorInvalidValue;
+    // extra columns of (groups * kv heads * prefix splits) workgroups, about 4 rows a wave
+    const int64_t per_col = int64_t{kWavesWg} * 4 * a.num_groups * a.num_kv_heads *
+                            (a.max_prefix_tokens / a.partition_tokens);
+    store_x = static_cast<int>(std::min<int64_t>((store.rows + per_col - 1) / per_col, 1024));
+    store_x = std::max(store_x, 1);
+  }
+  dim3 grid(tiles + store_x, a.num_groups * a.num_kv_heads, a.max_prefix_tokens / a.partition_tokens);
   hipLaunchKernelGGL((prefix_split_kernel<D, G>), grid, dim3(kWavesWg * kWave), lds, stream,
                      static_cast<const uint16_t*>(a.q), a.q_seq_stride, a.q_head_stride,
                      static_cast<const uint16_t*>(a.k_cache),
@@ -362,7 +384,7 @@ hipError_t run_prefix(const PrefixArgs& a, hipStream_t stream) {
                      a.block_table_stride, a.context_lens, a.prefix_group, a.prefix_tokens,
                      a.num_seqs, a.num_kv_heads, bs_log2, a.max_prefix_tokens,
                      a.partition_tokens, a.num_splits, a.scale * kLog2e, a.ws_acc, a.ws_ml,
-                     a.geom.block, a.geom.slot, a.geom.head);
+                     a.geom.block, a.geom.slot, a.geom.head, store, store_x);
   return hipGetLastError();
 }
 

@@ -55,6 +55,14 @@ bool aligned(const void* p, int64_t a, int64_t b, int64_t n) {
 
 }  // namespace
 
+bool store_rows_16(const StoreArgs& a, StoreRows* r) {
+  const int64_t eb = a.elt_bytes;
+  return aligned(a.k, a.k_tok_stride * eb, a.k_head_stride * eb, 16) &&
+         aligned(a.v, a.v_tok_stride * eb, a.v_head_stride * eb, 16) &&
+         reinterpret_cast<uintptr_t>(a.k_cache) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.v_cache) % 16 == 0 && store_rows_args<uint4>(a, r);
+}
+
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t eb = a.elt_bytes;
   const int64_t kt = a.k_tok_stride * eb, kh = a.k_head_stride * eb;

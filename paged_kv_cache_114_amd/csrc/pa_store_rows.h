@@ -15,11 +15,13 @@
 #pragma once
 
 #include "pa_common.h"
+#include "pa_internal.h"
 
 namespace pa {
 
 constexpr int kStoreUnroll = 2;  // words per lane whose loads are issued together
                                  // (a Qwen3 row of 8 heads x 128 bf16 is 2 per lane)
+                                 // -- the copy below is written for exactly 2
 
 struct StoreRows {
   const char* k;
@@ -34,6 +36,10 @@ struct StoreRows {
   int32_t bs_log2;
   int64_t block_b, slot_b, cache_head_b;  // cache strides, bytes
 };
+
+// The row-copy description of a store in 16-byte words (false: a shape or an
+// alignment the copy cannot take that way).
+bool store_rows_16(const StoreArgs& a, StoreRows* r);
 
 // Rows first_row, first_row + row_step, ... of the store, one per wave.
 template <typename W>
@@ -50,23 +56,25 @@ __device__ __forceinline__ void store_rows(const StoreRows& a, int first_row, in
     const int64_t head_b = is_v ? a.v_head_b : a.k_head_b;
     char* dst = (is_v ? a.v_cache : a.k_cache) + (slot >> a.bs_log2) * a.block_b +
                 (slot & bs_mask) * a.slot_b;
+    auto word = [&](int w) { return min(w, a.words_per_row - 1); };
+    auto src_at = [&](int w) {
+      return reinterpret_cast<const W*>(src + (w >> a.hw_log2) * head_b +
+                                        (w & hw_mask) * static_cast<int64_t>(sizeof(W)));
+    };
+    auto dst_at = [&](int w) {
+      return reinterpret_cast<W*>(dst + (w >> a.hw_log2) * a.cache_head_b +
+                                  (w & hw_mask) * static_cast<int64_t>(sizeof(W)));
+    };
     for (int w0 = 0; w0 < a.words_per_row; w0 += kStoreUnroll * kWave) {
       // No lane branches: a lane past the row re-reads its last word and writes
       // the same value back, so the loads issue back to back and the wave waits
-      // once before its stores.
-      W val[kStoreUnroll];
-#pragma unroll
-      for (int u = 0; u < kStoreUnroll; ++u) {
-        const int w = min(w0 + u * kWave + lane, a.words_per_row - 1);
-        val[u] = *reinterpret_cast<const W*>(src + (w >> a.hw_log2) * head_b +
-                                             (w & hw_mask) * static_cast<int64_t>(sizeof(W)));
-      }
-#pragma unroll
-      for (int u = 0; u < kStoreUnroll; ++u) {
-        const int w = min(w0 + u * kWave + lane, a.words_per_row - 1);
-        *reinterpret_cast<W*>(dst + (w >> a.hw_log2) * a.cache_head_b +
-                              (w & hw_mask) * static_cast<int64_t>(sizeof(W))) = val[u];
-      }
+      // once before its stores.  (Two named words, not an array: inside a large
+      // kernel an array here has been left in scratch memory.)
+      const int wa = word(w0 + lane), wb = word(w0 + kWave + lane);
+      const W va = *src_at(wa);
+      const W vb = *src_at(wb);
+      *dst_at(wa) = va;
+      *dst_at(wb) = vb;
     }
   }
 }
