@@ -162,16 +162,21 @@ int pa_qk_norm_rope_store(const void* qkv, int64_t qkv_tok_stride, const void* q
  * A decode of num_seqs sequences whose longest context is max_context_len,
  * cut into splits of partition_tokens logical positions, uses
  * num_splits = max(1, ceil(max_context_len / partition_tokens)) splits and a
- * workspace of num_seqs * num_q_heads * num_splits * (head_dim + 2) floats:
+ * workspace of
  *
- *   acc [num_seqs, num_q_heads, num_splits, head_dim]   then
- *   ml  [num_seqs, num_q_heads, num_splits, 2]
+ *   acc [num_seqs, num_q_heads, num_splits, head_dim] float   then
+ *   ml  [num_seqs, num_q_heads, num_splits, 2] float          then, from the
+ *       next 16-byte boundary,
+ *   list [1 + num_seqs * num_splits] int32 (rounded up to 16 bytes)
  *
  * acc is the split's un-normalised output sum_j 2^(t_j - m) v_j, ml holds
  * m = max_j t_j and l = sum_j 2^(t_j - m), where t_j = scale * log2(e) * q.k_j
  * is the score in base-2 units and j runs over the split's readable positions
  * [Intro §9.5, §13.3].  Splits at or past a sequence's context are not written.
- * partition_tokens must be a positive multiple of 64.
+ * list is pa_decode_shared_prefix's work list for its partition pass (a count,
+ * then the (sequence, split) pairs it computes), rewritten by every such call;
+ * no other call reads or writes it.  partition_tokens must be a positive
+ * multiple of 64.
  */
 int pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                              int32_t max_context_len, int32_t partition_tokens, size_t* bytes,

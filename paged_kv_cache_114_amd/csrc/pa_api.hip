@@ -122,7 +122,10 @@ int pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head
   int32_t s = (max_context_len + partition_tokens - 1) / partition_tokens;
   if (s < 1) s = 1;
   *num_splits = s;
-  *bytes = static_cast<size_t>(num_seqs) * num_q_heads * s * (head_dim + 2) * sizeof(float);
+  // the split statistics, then pa_decode_shared_prefix's work list (a count and
+  // one entry per (sequence, split))
+  *bytes = pa::decode_ws_stats_bytes(num_seqs, num_q_heads, s, head_dim) +
+           (static_cast<size_t>(num_seqs) * s * sizeof(int32_t) + sizeof(int32_t) + 15) / 16 * 16;
   return PA_OK;
 }
 
@@ -190,6 +193,9 @@ int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
   const pa::CacheGeom geom = geom_of(cache_layout, num_kv_heads, block_size, head_dim);
   // The shared-prefix pass runs only when some group can hold a whole split.
   const bool prefix = sp.group && sp.num_groups > 0 && sp.max_tokens >= partition_tokens;
+  int32_t* work_list = reinterpret_cast<int32_t*>(
+      static_cast<char*>(workspace) +
+      pa::decode_ws_stats_bytes(num_seqs, num_q_heads, splits, head_dim));
   NewRows rows = nr;
   if (prefix) {
     // This step's store runs in the prefix pass's launch (its rows lie past every
@@ -203,7 +209,7 @@ int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
                            block_table_stride, context_lens, sp.group, sp.tokens, sp.num_groups,
                            sp.max_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, partition_tokens, splits, scale, ws, ws + acc_elems,
-                           geom, nr.k ? &store : nullptr};
+                           geom, nr.k ? &store : nullptr, work_list, max_context_len};
     const int rc = launched(pa::launch_prefix_splits(pa_args, stream));
     if (rc != PA_OK) return rc;
     rows = NewRows{nullptr, nullptr, 0, 0, 0, 0, nullptr};
@@ -214,7 +220,8 @@ int decode_common(const void* q, int64_t q_seq_stride, int64_t q_head_stride,
                    ws + acc_elems, dtype == PA_DTYPE_BF16, geom, rows.k, rows.v,
                    rows.k_tok_stride, rows.k_head_stride, rows.v_tok_stride, rows.v_head_stride,
                    rows.slot_mapping, prefix ? sp.group : nullptr, prefix ? sp.tokens : nullptr,
-                   prefix ? sp.num_groups : 0, prefix ? sp.max_tokens : 0};
+                   prefix ? sp.num_groups : 0, prefix ? sp.max_tokens : 0,
+                   prefix ? work_list : nullptr};
   return launched(pa::launch_decode(a, stream));
 }
 

@@ -79,26 +79,35 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
     int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
     const int32_t* slot_mapping, T* k_cache_w, T* v_cache_w,
     const int32_t* __restrict__ prefix_group, const int32_t* __restrict__ prefix_tokens,
-    int32_t num_groups, int32_t max_prefix) {
+    int32_t num_groups, int32_t max_prefix, const int32_t* __restrict__ work_list) {
   using S = DecodeShape<T, D, G>;
   constexpr int kE = S::kE, kR = S::kR, kTpl = S::kTpl, kU = S::kU, kTile = S::kTile;
   extern __shared__ int32_t bt_lds[];
 
-  // Workgroups are handed to the 8 XCDs round-robin in launch order, and a
-  // sequence's later splits are empty when its context is short.  Rotating
-  // the sequence index by the split spreads every split level over all XCDs,
-  // so no XCD (with its own L2 and fabric share) ends up with most of the
-  // full splits.
-  // Split order: ascending, so that sequences holding the same blocks (a
-  // prefix-cache hit) read them at about the same time and share the caches;
-  // with prefix groups declared, those splits belong to the shared-prefix pass
-  // and members keep only their short tails, so the highest splits (full ones
-  // of the longest contexts) go first and the short ones fill the end of the
-  // pass (256 sequences, 192 of them sharing a 2048-token prefix: 312 -> 300
-  // us; the same batch without groups declared is 6% slower descending).
-  const int split = prefix_group ? static_cast<int>(gridDim.z) - 1 - static_cast<int>(blockIdx.z)
-                                 : static_cast<int>(blockIdx.z);
-  const int b = (blockIdx.x + num_seqs - split % num_seqs) % num_seqs;
+  // Without a work list: workgroups are handed to the 8 XCDs round-robin in
+  // launch order, and a sequence's later splits are empty when its context is
+  // short.  Rotating the sequence index by the split spreads every split level
+  // over all XCDs, so no XCD (with its own L2 and fabric share) ends up with
+  // most of the full splits.  The order is split-major and ascending, so that
+  // sequences holding the same blocks (a prefix-cache hit) read them at about
+  // the same time and share the caches.
+  // With a work list (prefix groups declared, whose prefix splits belong to
+  // the shared-prefix pass): workgroup column i takes entry i, the list holds
+  // only the splits this pass computes, full ones first and then the partial
+  // ones longest first, and columns past its end return.  Each entry is
+  // computed exactly as without the list.
+  int split, b;
+  if (work_list) {
+    const int i = blockIdx.x + gridDim.x * blockIdx.z;
+    if (i >= work_list[0]) return;  // uniform over the workgroup
+    const int e = work_list[1 + i];
+    b = e >> 16;
+    split = e & 0xffff;
+    if (b >= num_seqs || split >= num_splits) return;  // never for a list the library wrote
+  } else {
+    split = blockIdx.z;
+    b = (blockIdx.x + num_seqs - split % num_seqs) % num_seqs;
+  }
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int g = blockIdx.y * NW + wave;
@@ -379,7 +388,7 @@ hipError_t run_partition(const DecodeArgs& a, hipStream_t stream) {
                      a.k_tok_stride, a.k_head_stride, a.v_tok_stride, a.v_head_stride,
                      a.slot_mapping, static_cast<T*>(const_cast<void*>(a.k_cache)),
                      static_cast<T*>(const_cast<void*>(a.v_cache)), a.prefix_group,
-                     a.prefix_tokens, a.num_prefix_groups, a.max_prefix_tokens);
+                     a.prefix_tokens, a.num_prefix_groups, a.max_prefix_tokens, a.work_list);
   return hipGetLastError();
 }
 

@@ -58,6 +58,10 @@ struct DecodeArgs {
   const int32_t* prefix_group;
   const int32_t* prefix_tokens;
   int32_t num_prefix_groups, max_prefix_tokens;
+  // The partition pass's work list (nullptr: none): work_list[0] entries
+  // (sequence << 16 | split) from work_list[1] on, one per workgroup column,
+  // written by the shared-prefix pass's launch.
+  const int32_t* work_list;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
@@ -81,8 +85,17 @@ struct PrefixArgs {
   float* ws_ml;
   CacheGeom geom;
   const StoreArgs* store;  // non-null: this step's K/V store, by extra workgroups of the launch
+  int32_t* work_list;      // non-null: the partition pass's work list, by one extra workgroup
+  int32_t max_context_len;
 };
 hipError_t launch_prefix_splits(const PrefixArgs& a, hipStream_t stream);
+
+// Bytes of the decode workspace before the work list (16-byte aligned).
+inline size_t decode_ws_stats_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t num_splits,
+                                    int64_t head_dim) {
+  return (static_cast<size_t>(num_seqs * num_q_heads * num_splits * (head_dim + 2)) *
+              sizeof(float) + 15) / 16 * 16;
+}
 
 struct ReduceArgs {
   const float* ws_acc;

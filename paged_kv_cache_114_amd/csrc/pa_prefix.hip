@@ -84,6 +84,65 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// The partition pass's work list for this call, built by one workgroup: the
+// (sequence, split) pairs that pass computes -- splits [lo, n) of sequence b,
+// n = ceil(L / P) for its context L (cut to max_ctx), lo the first split the
+// shared-prefix pass does not take (the partition kernel's own skip rule) --
+// full splits first, then the partial last splits longest first (32 length
+// classes), so the hardware hands out the longest work first and the short
+// splits fill the end.  list[0] is the count; entries are b << 16 | split.
+// Order within a class follows the atomics and does not matter: every entry
+// is computed the same wherever it sits.
+__device__ __forceinline__ void build_work_list(
+    int32_t* __restrict__ list, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ prefix_group, const int32_t* __restrict__ prefix_tokens,
+    int32_t num_seqs, int32_t num_groups, int32_t max_prefix, int32_t max_ctx, int32_t P) {
+  constexpr int kClasses = 33;  // 0: full splits; 1..32: partial, longest first
+  __shared__ int count[kClasses], offset[kClasses];
+  const int tid = threadIdx.x;
+  if (tid < kClasses) count[tid] = 0;
+  __syncthreads();
+  auto range = [&](int b, int& lo, int& n, int& tail) {
+    const int ctx = min(context_lens[b], max_ctx);
+    n = ctx > 0 ? (ctx + P - 1) / P : 0;
+    const int grp = prefix_group[b];
+    lo = n > 0 && static_cast<unsigned>(grp) < static_cast<unsigned>(num_groups)
+             ? max(min(min(prefix_tokens[grp], max_prefix) / P, (ctx - 1) / P), 0)
+             : 0;
+    tail = ctx - (n - 1) * P;  // 1 .. P when n > 0
+  };
+  auto cls = [&](int tail) { return 1 + (P - 1 - tail) * 32 / P; };  // 1 .. 32 for tail < P
+  for (int b = tid; b < num_seqs; b += blockDim.x) {
+    int lo, n, tail;
+    range(b, lo, n, tail);
+    if (n <= lo) continue;
+    const int full = tail == P ? n - lo : n - 1 - lo;
+    if (full > 0) atomicAdd(&count[0], full);
+    if (tail < P) atomicAdd(&count[cls(tail)], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int total = 0;
+    for (int c = 0; c < kClasses; ++c) {
+      offset[c] = total;
+      total += count[c];
+    }
+    list[0] = total;
+  }
+  __syncthreads();
+  for (int b = tid; b < num_seqs; b += blockDim.x) {
+    int lo, n, tail;
+    range(b, lo, n, tail);
+    if (n <= lo) continue;
+    const int full = tail == P ? n - lo : n - 1 - lo;
+    if (full > 0) {
+      const int at = atomicAdd(&offset[0], full);
+      for (int k = 0; k < full; ++k) list[1 + at + k] = (b << 16) | (lo + k);
+    }
+    if (tail < P) list[1 + atomicAdd(&offset[cls(tail)], 1)] = (b << 16) | (n - 1);
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kWavesWg * kWave) void prefix_split_kernel(
     const uint16_t* __restrict__ q, int64_t q_seq_stride, int64_t q_head_stride,
@@ -94,7 +153,7 @@ __global__ __launch_bounds__(kWavesWg * kWave) void prefix_split_kernel(
     int32_t bs_log2, int32_t max_prefix, int32_t partition_tokens, int32_t num_splits,
     float scale_log2, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     int64_t block_stride, int64_t slot_stride, int64_t head_stride, StoreRows store,
-    int32_t store_x) {
+    int32_t store_x, int32_t* __restrict__ work_list, int32_t max_ctx) {
   using S = PrefixShape<D>;
   constexpr int kMembers = kRowsWg / G;  // members per workgroup
   __shared__ __attribute__((aligned(1024))) uint16_t region[kWavesWg][S::kRegionElems];
@@ -112,6 +171,16 @@ __global__ __launch_bounds__(kWavesWg * kWave) void prefix_split_kernel(
   // The last store_x columns of the grid copy this step's K/V rows into the
   // cache instead (none when store.rows is 0); a stored row is never a slot
   // this pass reads (the new positions lie past every group's prefix).
+  // The column before them builds the partition pass's work list (its first
+  // workgroup; the others return).
+  const int plan_x = work_list ? 1 : 0;
+  if (plan_x && static_cast<int>(blockIdx.x) == static_cast<int>(gridDim.x) - store_x - 1) {
+    if (blockIdx.y == 0 && blockIdx.z == 0)
+      build_work_list(work_list, context_lens, prefix_group, prefix_tokens, num_seqs,
+                      static_cast<int>(gridDim.y) / num_kv_heads, max_prefix, max_ctx,
+                      partition_tokens);
+    return;
+  }
   if (static_cast<int>(blockIdx.x) >= static_cast<int>(gridDim.x) - store_x) {
     const int wg = blockIdx.x - (gridDim.x - store_x) + store_x * (blockIdx.y + gridDim.y * blockIdx.z);
     store_rows<uint4>(store, wg * kWavesWg + wave, store_x * gridDim.y * gridDim.z * kWavesWg);
@@ -376,7 +445,8 @@ hipError_t run_prefix(const PrefixArgs& a, hipStream_t stream) {
     store_x = static_cast<int>(std::min<int64_t>((store.rows + per_col - 1) / per_col, 1024));
     store_x = std::max(store_x, 1);
   }
-  dim3 grid(tiles + store_x, a.num_groups * a.num_kv_heads, a.max_prefix_tokens / a.partition_tokens);
+  dim3 grid(tiles + (a.work_list ? 1 : 0) + store_x, a.num_groups * a.num_kv_heads,
+            a.max_prefix_tokens / a.partition_tokens);
   hipLaunchKernelGGL((prefix_split_kernel<D, G>), grid, dim3(kWavesWg * kWave), lds, stream,
                      static_cast<const uint16_t*>(a.q), a.q_seq_stride, a.q_head_stride,
                      static_cast<const uint16_t*>(a.k_cache),
@@ -384,7 +454,8 @@ hipError_t run_prefix(const PrefixArgs& a, hipStream_t stream) {
                      a.block_table_stride, a.context_lens, a.prefix_group, a.prefix_tokens,
                      a.num_seqs, a.num_kv_heads, bs_log2, a.max_prefix_tokens,
                      a.partition_tokens, a.num_splits, a.scale * kLog2e, a.ws_acc, a.ws_ml,
-                     a.geom.block, a.geom.slot, a.geom.head, store, store_x);
+                     a.geom.block, a.geom.slot, a.geom.head, store, store_x, a.work_list,
+                     a.max_context_len);
   return hipGetLastError();
 }
 

@@ -22,7 +22,9 @@ int main(void) {
   size_t bytes = 0;
   int32_t splits = 0;
   EXPECT(pa_decode_workspace_size(512, 16, 128, 4096, 1024, &bytes, &splits) == PA_OK);
-  EXPECT(splits == 4 && bytes == (size_t)512 * 16 * 4 * 130 * 4);
+  /* split statistics, then the shared-prefix work list (count + one int32 per
+     (sequence, split)), each rounded up to 16 bytes */
+  EXPECT(splits == 4 && bytes == (size_t)512 * 16 * 4 * 130 * 4 + (4 * (512 * 4 + 1) + 15) / 16 * 16);
   EXPECT(pa_decode_workspace_size(1, 2, 64, 37, 100, &bytes, &splits) == PA_ERR_UNSUPPORTED);
   EXPECT(pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 0, &bytes, &splits) == PA_OK);
   EXPECT(splits == 1 && bytes > 0);

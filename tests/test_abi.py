@@ -43,11 +43,18 @@ def test_version_and_strerror():
     assert pa.strerror(12345) == "unknown status"
 
 
+def _up16(n):
+    return (n + 15) // 16 * 16
+
+
 def test_workspace_size_formula():
+    # the split statistics (acc and (m, l) per sequence, query head and split),
+    # then the shared-prefix call's work list (a count and one int32 per
+    # (sequence, split)), each rounded up to 16 bytes
     nbytes, splits = pa.pa_decode_workspace_size(512, 16, 128, 4096, 1024)
-    assert splits == 4 and nbytes == 512 * 16 * 4 * 130 * 4
+    assert splits == 4 and nbytes == _up16(512 * 16 * 4 * 130 * 4) + _up16(4 * (512 * 4 + 1))
     nbytes, splits = pa.pa_decode_workspace_size(3, 2, 64, 0, 512)
-    assert splits == 1 and nbytes == 3 * 2 * 1 * 66 * 4
+    assert splits == 1 and nbytes == _up16(3 * 2 * 1 * 66 * 4) + _up16(4 * (3 * 1 + 1))
     nbytes, splits = pa.pa_decode_workspace_size(1, 2, 64, 37, 64)
     assert splits == 1
     _, splits = pa.pa_decode_workspace_size(1, 2, 64, 65, 64)
