@@ -578,7 +578,10 @@ def roofline(run, t, name):
                     "profile of the same kernel source (profiles/hbm_traffic.json); null when the "
                     "source changed since")
     if run.kind == "decode":
-        fused_launch = run.fused_store and run.store_fused_in_launch()
+        # pa_decode_shared_prefix stores in its prefix pass's launch whatever the grid;
+        # pa_store_decode stores in the partition launch when the fused kernel keeps the
+        # grid resident, else in a launch of its own before it
+        fused_launch = run.fused_store and (run.shared_prefix or run.store_fused_in_launch())
         if amortize:
             kernel_ms = run.main_kernel_amortized(fused=fused_launch)
             timing = ("HIP events around 16 back-to-back launches on 16 pool copies after a "
@@ -594,9 +597,9 @@ def roofline(run, t, name):
             alg = run.case.kv_bytes_unique() + (run.store_bytes() if fused_launch else 0)
             traffic = measured_traffic(name + "_shared_prefix",
                                        kname + ("" if fused_launch else "_plain"))
-            kdesc = ("pa_decode_shared_prefix: prefix_split_kernel + " + kname +
-                     (" (with the fused store)" if fused_launch else
-                      " (plain; this step stores its rows in a launch of its own)"))
+            kdesc = ("pa_decode_shared_prefix: prefix_split_kernel (the prefix splits" +
+                     (", this step's store" if fused_launch else "") +
+                     " and the partition pass's work list) + " + kname + " (plain)")
         else:
             alg = run.kv_bytes() + (run.store_bytes() if fused_launch else 0)
             traffic = measured_traffic(name, kname + ("" if fused_launch else "_plain"))
