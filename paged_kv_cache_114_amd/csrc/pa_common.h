@@ -31,11 +31,19 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// Two values at once (lo in the low half): one v_cvt_pk_bf16_f32.  Its bits
+// equal the integer rounding (add 0x7fff plus the kept lsb, NaN quieted by
+// setting bit 6) on every class of input -- ties, near-ties, denormals,
+// infinities, values that round to infinity, NaN payloads -- checked on the
+// GPU; the integer form, written out, cost ~10 instructions a value with its
+// NaN branch.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(f32x2_to_bf16x2_rne(f, 0.f));
 }
 
 // Widen the 16 bytes one lane holds into fp32 values.

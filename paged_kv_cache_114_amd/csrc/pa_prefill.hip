@@ -849,10 +849,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int dim = db * 32 + 8 * r4 + 4 * half;
-      const uint32_t lo = f32_to_bf16_rne(acc_o[db][4 * r4 + 0] * inv) |
-                          (static_cast<uint32_t>(f32_to_bf16_rne(acc_o[db][4 * r4 + 1] * inv)) << 16);
-      const uint32_t hi = f32_to_bf16_rne(acc_o[db][4 * r4 + 2] * inv) |
-                          (static_cast<uint32_t>(f32_to_bf16_rne(acc_o[db][4 * r4 + 3] * inv)) << 16);
+      const uint32_t lo = f32x2_to_bf16x2_rne(acc_o[db][4 * r4 + 0] * inv, acc_o[db][4 * r4 + 1] * inv);
+      const uint32_t hi = f32x2_to_bf16x2_rne(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv);
       *reinterpret_cast<uint2*>(op + dim) = make_uint2(lo, hi);
     }
   }
@@ -1080,10 +1078,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
     o.w = fmaf(w, v.w, o.w);
   }
   const float inv = 1.f / l;
-  const uint32_t lo = f32_to_bf16_rne(o.x * inv) |
-                      (static_cast<uint32_t>(f32_to_bf16_rne(o.y * inv)) << 16);
-  const uint32_t hi = f32_to_bf16_rne(o.z * inv) |
-                      (static_cast<uint32_t>(f32_to_bf16_rne(o.w * inv)) << 16);
+  const uint32_t lo = f32x2_to_bf16x2_rne(o.x * inv, o.y * inv);
+  const uint32_t hi = f32x2_to_bf16x2_rne(o.z * inv, o.w * inv);
   *reinterpret_cast<uint2*>(out + row * out_tok_stride + head * out_head_stride + 4 * c) =
       make_uint2(lo, hi);
   }
