@@ -179,6 +179,44 @@ def test_shared_prefix_block_larger_than_split():
     check(case, 64)
 
 
+@pytest.mark.parametrize("partition,store", [(64, True), (64, False), (128, True)])
+def test_shared_prefix_work_list_boundaries(partition, store):
+    """The partition pass's work list at its edges: contexts ending exactly on a split
+    boundary (a full last split), one token, one short of and one past a boundary,
+    exactly max_context_len and a multiple of the split, members one and two splits
+    past their prefix and one a token past it, a padding row, and a declared group
+    that has no members."""
+    lengths = [256 + 64, 256 + 128, 256 + 1, 64, 128, 1, 1024, 63, 65]
+    case = W.decode_case(f"list_edges_{partition}", 5600, bs=64, lengths=lengths, pad_rows=1,
+                         prefix_groups=[(256, [0, 1, 2]), (128, [])])
+    check(case, partition, store)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_prefix_work_list_random_batches(seed):
+    """Random batches: up to three groups of random prefix lengths and sizes among
+    private sequences of random lengths, random split sizes; every split the partition
+    pass computes is compared bit for bit with pa_store_decode's (so a split missing
+    from the list would show as the workspace's NaN fill)."""
+    rng = np.random.default_rng(7000 + seed)
+    bs = int(rng.choice([16, 64]))
+    n = int(rng.integers(20, 90))
+    order = rng.permutation(n)
+    groups, at = [], 0
+    for _ in range(int(rng.integers(1, 4))):
+        prefix = bs * int(rng.integers(1, 40))
+        size = int(rng.integers(1, 20))
+        groups.append((prefix, sorted(int(b) for b in order[at:at + size])))
+        at += size
+    lengths = rng.integers(1, 2500, size=n)
+    for prefix, members in groups:
+        for b in members:  # the newest token past the prefix (the call's precondition)
+            lengths[b] = prefix + int(rng.integers(1, 1200))
+    case = W.decode_case(f"list_random_{seed}", 7100 + seed, bs=bs, lengths=lengths,
+                         pad_rows=int(rng.integers(0, 2)), prefix_groups=groups)
+    check(case, int(rng.choice([64, 128, 256, 512])), oracle_seqs=sample_seqs(case, 6, seed))
+
+
 def test_shared_prefix_statistics_match_oracle():
     """The MFMA pass alone: (m, l, acc) of every prefix split equals the oracle's split
     statistics, in the base-2 units of the workspace."""
