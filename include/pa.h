@@ -284,9 +284,14 @@ int pa_store_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
  * the pass launches ceil(num_seqs * G / 32) x (num_groups * num_kv_heads) x
  * (max_prefix_tokens / partition_tokens) workgroups, of which those past a
  * group's members or prefix return at once, so it suits batches with a few
- * groups.  With num_groups = 0 (or max_prefix_tokens < partition_tokens) this
- * is pa_decode / pa_store_decode.  bf16 only (PA_ERR_UNSUPPORTED otherwise);
- * every other argument and the error behaviour are as for pa_store_decode.
+ * groups.  The same launch carries this step's store (when asked for) and
+ * writes the partition pass's work list to the workspace's tail (see
+ * pa_decode_workspace_size): the (sequence, split) pairs that pass computes,
+ * full splits first and then the partial ones longest first, which the
+ * partition launch then takes in that order.  With num_groups = 0 (or
+ * max_prefix_tokens < partition_tokens) this is pa_decode / pa_store_decode.
+ * bf16 only (PA_ERR_UNSUPPORTED otherwise); every other argument and the error
+ * behaviour are as for pa_store_decode.
  */
 int pa_decode_shared_prefix(const void* k_new, const void* v_new, int64_t k_tok_stride,
                             int64_t k_head_stride, int64_t v_tok_stride, int64_t v_head_stride,
