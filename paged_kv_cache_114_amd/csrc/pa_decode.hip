@@ -334,6 +334,20 @@ __global__ __launch_bounds__(4 * kWave) void decode_reduce_kernel(
   const int ctx = context_lens[b];
   const int ns = min(num_splits, (ctx + partition_tokens - 1) / partition_tokens);
 
+  // The next kMid splits are loaded in one batch with the maximum's loads (they
+  // do not depend on it), so a row of up to kPre + kMid splits costs two round
+  // trips to memory; further splits go kMid at a time.  Splits are combined in
+  // ascending order whatever the batching.
+  constexpr int kMid = 12;
+  float2 st2[kMid];
+  float part2[kMid][kDpl];
+#pragma unroll
+  for (int j = 0; j < kMid; ++j)
+    if (kPre + j < ns) {
+      st2[j] = ml[kPre + j];
+#pragma unroll
+      for (int k = 0; k < kDpl; ++k) part2[j][k] = acc[static_cast<int64_t>(kPre + j) * D + k];
+    }
   float m_star = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kPre; ++s)
@@ -352,12 +366,30 @@ __global__ __launch_bounds__(4 * kWave) void decode_reduce_kernel(
 #pragma unroll
       for (int k = 0; k < kDpl; ++k) o[k] = fmaf(w, part[s][k], o[k]);
     }
-  for (int s = kPre; s < ns; ++s) {
-    const float2 sm = ml[s];
-    const float w = fast_exp2(sm.x - m_star);
-    lsum = fmaf(w, sm.y, lsum);
 #pragma unroll
-    for (int k = 0; k < kDpl; ++k) o[k] = fmaf(w, acc[static_cast<int64_t>(s) * D + k], o[k]);
+  for (int j = 0; j < kMid; ++j)
+    if (kPre + j < ns) {
+      const float w = fast_exp2(st2[j].x - m_star);
+      lsum = fmaf(w, st2[j].y, lsum);
+#pragma unroll
+      for (int k = 0; k < kDpl; ++k) o[k] = fmaf(w, part2[j][k], o[k]);
+    }
+  for (int s0 = kPre + kMid; s0 < ns; s0 += kMid) {
+#pragma unroll
+    for (int j = 0; j < kMid; ++j)
+      if (s0 + j < ns) {
+        st2[j] = ml[s0 + j];
+#pragma unroll
+        for (int k = 0; k < kDpl; ++k) part2[j][k] = acc[static_cast<int64_t>(s0 + j) * D + k];
+      }
+#pragma unroll
+    for (int j = 0; j < kMid; ++j)
+      if (s0 + j < ns) {
+        const float w = fast_exp2(st2[j].x - m_star);
+        lsum = fmaf(w, st2[j].y, lsum);
+#pragma unroll
+        for (int k = 0; k < kDpl; ++k) o[k] = fmaf(w, part2[j][k], o[k]);
+      }
   }
   const float inv = ns > 0 ? 1.f / lsum : 0.f;
   T* dst = out + static_cast<int64_t>(b) * out_seq_stride + static_cast<int64_t>(h) * out_head_stride +

@@ -189,11 +189,17 @@ def test_workspace_partials_match_oracle_split_statistics():
                 assert np.all(np.abs(acc[b, h, s] - a) <= 1e-4 * (np.abs(a) + l) + 1e-5)
 
 
-def test_reduce_on_synthetic_partials():
+@pytest.mark.parametrize("s_,lens", [
+    (7, [0, 1, 64, 65, 7 * 64]),
+    # 40 splits: rows of 0, 1, 16 (the first two load batches), 17 and 29 (one and
+    # two more batches) and 40 active splits
+    (40, [0, 1, 16 * 64, 16 * 64 + 1, 28 * 64 + 5, 40 * 64]),
+])
+def test_reduce_on_synthetic_partials(s_, lens):
     """pa_decode_reduce alone, on random split statistics, against oracle.merge."""
-    rng = np.random.default_rng(9)
-    b_, hq, d, s_, p = 5, 4, 128, 7, 64
-    ctx = np.array([0, 1, 64, 65, 7 * 64], np.int32)
+    rng = np.random.default_rng(9 + s_)
+    b_, hq, d, p = len(lens), 4, 128, 64
+    ctx = np.array(lens, np.int32)
     m = rng.normal(0, 20, size=(b_, hq, s_)).astype(np.float32)
     l = rng.uniform(0.5, 64, size=(b_, hq, s_)).astype(np.float32)
     acc = (rng.normal(size=(b_, hq, s_, d)) * l[..., None]).astype(np.float32)
