@@ -78,9 +78,10 @@ def test_prefill_mixed_engine_batch(name):
 @pytest.mark.parametrize("name", ["c3", "mixed"])
 def test_prefill_rounded_p_rows_keep_a_margin(name):
     """Rows that see at least 256 keys put p into P.V rounded to nearest bf16 (no
-    remainder).  On the benchmark batches their worst error stays below half of the
-    2e-3 + 1e-2 |ref| bound (measured about a quarter); rows with fewer keys carry
-    the remainder and stay within the bound as every other test checks."""
+    remainder).  On these batches their worst error stays below half of the
+    2e-3 + 1e-2 |ref| bound (measured 0.47 on C3, 0.40 on the mixed batch; the kernel
+    is deterministic, so these are fixed values); rows with fewer keys carry the
+    remainder and stay within the bound as every other test checks."""
     from pa_runner import tolerance
     case = W.FULL_CASES[name]()
     _, vals, out, (host, ref) = _prefill_vs_oracle(case)
@@ -89,6 +90,8 @@ def test_prefill_rounded_p_rows_keep_a_margin(name):
     long_rows = (pos + 1 >= 256)[host.token_rows]
     assert long_rows.sum() > len(long_rows) // 2
     ratio = np.abs(got - ref) / tolerance(ref, case.dtype)
+    print(f"{case.name}: worst error / bound, rows with >= 256 keys {float(ratio[long_rows].max()):.3f}, "
+          f"other rows {float(ratio[~long_rows].max()) if (~long_rows).any() else 0.0:.3f}", flush=True)
     assert float(ratio[long_rows].max()) < 0.5, float(ratio[long_rows].max())
 
 
