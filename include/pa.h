@@ -368,8 +368,8 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
  * position (a decode row of a mixed batch) is never cut: its item reads its
  * keys decode-style, split over the workgroup's waves.  With S = ceil(max_seqlen_k /
  * split_keys) (S = 1 when split_keys is 0, the no-split setting) the
- * workspace holds, in order and 256-byte aligned: the work-list counter
- * (256 bytes), the work list ((ceil(total_q / R) + num_seqs) * S *
+ * workspace holds, in order and 256-byte aligned: the work-list counters
+ * (512 bytes), the work list ((ceil(total_q / R) + num_seqs) * S *
  * num_kv_heads entries of 8 bytes, R = 32 * max(1, 4 / group) query rows per
  * tile), and when S > 1 the list of split query tiles ((ceil(total_q / R) +
  * num_seqs) entries of 8 bytes) and

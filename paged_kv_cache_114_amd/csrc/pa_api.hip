@@ -375,9 +375,10 @@ int pa_decode_reduce(const void* workspace, size_t workspace_bytes, const int32_
 
 namespace {
 
-// Prefill workspace layout (bytes): [0, 256) ticket counter and work-list
-// length; the work list (int2 per item, capacity items); then, when tiles are
-// split, acc [S, total_q, Hq, D] and ml [S, total_q, Hq, 2] floats.
+// Prefill workspace layout (bytes): [0, kPrefillTicketBytes) the work-list
+// counters; the work list (int2 per item, capacity items); then, when tiles
+// are split, the split tiles and acc [S, total_q, Hq, D] and ml [S, total_q,
+// Hq, 2] floats.
 struct PrefillLayout {
   size_t items_off, merges_off, acc_off, ml_off, bytes;
 };
@@ -389,7 +390,7 @@ PrefillLayout prefill_layout(int32_t num_seqs, int32_t total_q, int32_t num_q_he
   const size_t tiles = static_cast<size_t>((total_q + rows - 1) / rows + num_seqs);
   const size_t capacity = tiles * splits * num_kv_heads;
   PrefillLayout l;
-  l.items_off = 256;
+  l.items_off = pa::kPrefillTicketBytes;
   l.merges_off = round256(l.items_off + capacity * 8);
   l.acc_off = round256(l.merges_off + (splits > 1 ? tiles * 8 : 0));
   const size_t slots = splits > 1 ? static_cast<size_t>(splits) * total_q * num_q_heads : 0;

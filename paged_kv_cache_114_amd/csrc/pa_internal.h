@@ -108,6 +108,10 @@ struct ReduceArgs {
 };
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 
+// The prefill workspace opens with this many bytes of work-list counters
+// (claim counter, entry count, finished workgroups) ahead of the work list.
+constexpr size_t kPrefillTicketBytes = 512;
+
 struct PrefillArgs {
   const void* q;
   int64_t q_tok_stride, q_head_stride;
@@ -121,7 +125,7 @@ struct PrefillArgs {
   int32_t max_seqlen_q, max_seqlen_k, total_q;
   float scale;
   int32_t split_keys, num_splits;  // num_splits == 1: no split, ws_acc / ws_ml unused
-  uint32_t* tickets;               // work-list counter and length
+  uint32_t* tickets;               // work-list counters and length (kPrefillTicketBytes)
   int2* items;                     // work list written by the plan kernel
   int2* merges;                    // split query tiles, written by the plan kernel
   float* ws_acc;                   // [S, total_q, Hq, D]

@@ -67,6 +67,14 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBN = 64;  // keys per tile
+// The work-list counters open the workspace: tickets[0] the claim counter,
+// tickets[1] the number of entries, tickets[2] the number of split tiles, and
+// in a 256-byte chunk of its own tickets[kTicketExit], the count of
+// workgroups that have left.  Every workgroup's last claim and its exit meet
+// at the end of the kernel, and atomics on different words of one line
+// serialise behind each other.
+constexpr int kTicketExit = 64;
+static_assert((kTicketExit + 1) * 4 <= kPrefillTicketBytes, "exit counter fits the ticket area");
 // Rows whose first position sees fewer keys than this carry the remainder of
 // p through P.V (see short_rows).
 constexpr int kRestKeys = 256;
@@ -858,9 +866,9 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
   // The last workgroup to leave resets the claim counter (every other one has
   // made its final claim before it counted itself out), so the work list can
   // serve the next call with the same metadata without being rebuilt.
-  if (tid == 0 && atomicAdd(&tickets[3], 1u) == gridDim.x - 1) {
+  if (tid == 0 && atomicAdd(&tickets[kTicketExit], 1u) == gridDim.x - 1) {
     atomicExch(&tickets[0], 0u);
-    atomicExch(&tickets[3], 0u);
+    atomicExch(&tickets[kTicketExit], 0u);
   }
 }
 
@@ -869,8 +877,9 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
 // of key tiles the entry covers, largest first (a counting sort; the order
 // among equal weights is arbitrary and does not change any result), the kv
 // heads of one (tile, range) adjacent.  tickets[0] is the claim counter, reset
-// here; tickets[1] the number of entries; tickets[2] the number of split
-// query tiles, listed in merges[] for the merge kernel.
+// here (and by the tile kernel's last workgroup); tickets[1] the number of
+// entries; tickets[2] the number of split query tiles, listed in merges[] for
+// the merge kernel.
 constexpr int kPlanThreads = 1024;
 // A decode row's item weighs its key tiles divided by this (its waves split the
 // keys and do no MFMA work), for the largest-first order.
@@ -999,7 +1008,7 @@ __device__ __forceinline__ void plan_body(
     tickets[0] = 0u;
     tickets[1] = static_cast<uint32_t>(n_entries);
     tickets[2] = static_cast<uint32_t>(n_merges);
-    tickets[3] = 0u;  // workgroups of the tile kernel that have left
+    tickets[kTicketExit] = 0u;  // workgroups of the tile kernel that have left
   }
 }
 

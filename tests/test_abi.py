@@ -174,18 +174,18 @@ def test_prefill_validation():
 
 def test_prefill_workspace_size_formula():
     r256 = lambda x: (x + 255) // 256 * 256
-    # group 2: 64-row tiles; no split -> counter + work list only
+    # group 2: 64-row tiles; no split -> counters (512 bytes) + work list only
     nbytes, splits = pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 0)
-    assert splits == 1 and nbytes == r256(256 + ((6000 + 63) // 64 + 8) * 8 * 8)
+    assert splits == 1 and nbytes == r256(512 + ((6000 + 63) // 64 + 8) * 8 * 8)
     assert pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 2048)[1] == 1
     nbytes, splits = pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, 768)
-    items = r256(256 + ((6000 + 63) // 64 + 8) * 3 * 8 * 8)
+    items = r256(512 + ((6000 + 63) // 64 + 8) * 3 * 8 * 8)
     merges = r256(items + ((6000 + 63) // 64 + 8) * 8)
     acc = r256(merges + 3 * 6000 * 16 * 128 * 4)
     assert splits == 3 and nbytes == r256(acc + 3 * 6000 * 16 * 2 * 4)
     # group 8: 32-row tiles
     nbytes, _ = pa.pa_prefill_workspace_size(2, 100, 16, 2, 64, 100, 0)
-    assert nbytes == r256(256 + (4 + 2) * 2 * 8)
+    assert nbytes == r256(512 + (4 + 2) * 2 * 8)
     for bad in (100, -64):
         with pytest.raises(pa.PAError):
             pa.pa_prefill_workspace_size(8, 6000, 16, 8, 128, 2048, bad)
