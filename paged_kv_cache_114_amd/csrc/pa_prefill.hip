@@ -834,7 +834,8 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
     key_loop(std::false_type{});
 
   const float l_tot = l_run + lane_xor32(l_run);
-  if (row_ok && n_split > 1) {
+  if (n_split > 1) {
+  if (row_ok) {
     // Partial result of this key range, against its own reference maximum:
     // acc [split][row][head][D] un-normalised, ml [split][row][head] = (m, l).
     const int64_t slot =
@@ -848,19 +849,47 @@ __global__ __launch_bounds__((PrefillShape<D, G>::kThreads), 2) void prefill_ker
             make_float4(acc_o[db][4 * r4], acc_o[db][4 * r4 + 1], acc_o[db][4 * r4 + 2],
                         acc_o[db][4 * r4 + 3]);
     if (half == 0) reinterpret_cast<float2*>(ws_ml)[slot] = make_float2(m_ref, l_tot);
-  } else if (row_ok) {
+  }
+  } else {
+  // The wave's 32 x D output tile goes out through LDS so that every store
+  // writes whole rows, 16 bytes a lane: written straight from the registers,
+  // a lane holds 8 bytes of a row and each store would touch 32 rows 4 KB
+  // apart.  The K/V tile buffers are idle once the last tile's barrier has
+  // passed; each holds two waves' tiles, row-major with the 16-byte chunk
+  // index XOR-swizzled by the row against bank conflicts.  Rows past the
+  // sequence's end are staged (whatever they hold) but not stored.
+  constexpr int kC = D / 8;  // 16-byte chunks per row
+  static_assert(S::kWaves <= 8, "two staged tiles per K/V buffer");
+  uint16_t* const buf = wave < 4 ? (wave < 2 ? k_lds0 : k_lds1) : (wave < 6 ? v_lds0 : v_lds1);
+  char* const stage = reinterpret_cast<char*>(buf) + (wave % 2) * (32 * D * 2);
+  // The lane index is made opaque here so that the staging addresses, which
+  // are the same for every item, are computed here instead of being hoisted
+  // out of the item loop into registers the tile loop needs.
+  int sl = lane;
+  asm volatile("" : "+v"(sl));
+  const int s_col = sl % 32, s_half = sl / 32;
   const float inv = 1.f / l_tot;
-  uint16_t* op = out + static_cast<int64_t>(q_begin + my_row) * out_tok_stride +
-                 static_cast<int64_t>(head) * out_head_stride;
 #pragma unroll
   for (int db = 0; db < S::kDB; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int dim = db * 32 + 8 * r4 + 4 * half;
+      const int chunk = 4 * db + r4;  // dims db * 32 + 8 * r4 .. + 7
       const uint32_t lo = f32x2_to_bf16x2_rne(acc_o[db][4 * r4 + 0] * inv, acc_o[db][4 * r4 + 1] * inv);
       const uint32_t hi = f32x2_to_bf16x2_rne(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + dim) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(stage + s_col * (2 * D) + ((chunk ^ (s_col % kC)) * 16) +
+                                8 * s_half) = make_uint2(lo, hi);
     }
+  __syncthreads();  // n_split is the workgroup's: every wave is here
+  constexpr int kRowsPer = kWave / kC;  // rows one wave-wide read covers
+  const int c = sl % kC;
+#pragma unroll
+  for (int i = 0; i < 32 / kRowsPer; ++i) {
+    const int r = i * kRowsPer + sl / kC;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + r * (2 * D) + ((c ^ (r % kC)) * 16));
+    if (w_q0 + r < lq)
+      *reinterpret_cast<uint4*>(out + static_cast<int64_t>(q_begin + w_q0 + r) * out_tok_stride +
+                                static_cast<int64_t>(head) * out_head_stride + c * 8) = v;
+  }
   }
   }  // next item
   // The last workgroup to leave resets the claim counter (every other one has
