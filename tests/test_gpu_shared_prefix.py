@@ -284,21 +284,27 @@ def test_shared_prefix_full_c5_timed_partition():
     check(case, p, True, sorted(pick))
 
 
-def test_shared_prefix_graph_replays_equal_eager():
+@pytest.mark.parametrize("store", [False, True])
+def test_shared_prefix_graph_replays_equal_eager(store):
     """Captured in a HIP graph, the step (the prefix pass, the partition pass, the
     reduce) replays the eager result bit for bit, three times with eager work between
-    the replays and once after new queries."""
+    the replays and once after new queries.  With the store (which runs in the
+    prefix pass's launch), each call writes the same rows to the same slots again."""
     case = W.SMALL_CASES["c5s"]()
     p = 128
+    print(f"shared_prefix graph case={case.name} P={p} store={store}", flush=True)
     vals = W.materialize(case, DEV)
-    run_store(vals)  # the step's rows stored once; the captured step only reads the pool
+    if not store:
+        run_store(vals)  # the step's rows stored once; the captured step only reads the pool
+    new = dict(k_new=vals["k_new"], v_new=vals["v_new"],
+               slot_mapping=vals["slot_mapping"]) if store else {}
     ws, out, splits = decode_buffers(case, p)
 
     def step():
         pa.pa_decode_shared_prefix(vals["q"], vals["k_cache"], vals["v_cache"],
                                    vals["block_table"], vals["context_lens"],
                                    vals["prefix_group"], vals["prefix_tokens"], max_prefix(case),
-                                   case.max_context_len, p, case.scale, ws)
+                                   case.max_context_len, p, case.scale, ws, **new)
         pa.pa_decode_reduce(ws, vals["context_lens"], splits, p, out)
 
     step()
