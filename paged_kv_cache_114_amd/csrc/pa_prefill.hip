@@ -915,6 +915,20 @@ constexpr int kPlanThreads = 1024;
 constexpr int kDecodeRowShare = 4;
 constexpr int kPlanBins = 1024;  // weights >= kPlanBins - 1 share the last bin
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP moves: shifts right
+// by 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside
+// the row read 0), then lane 15 added into rows 1 and 3 and lane 31 into rows
+// 2 and 3.  Lanes a move does not write get `old`, here 0.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 template <int BM>
 __device__ __forceinline__ void plan_body(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t num_seqs,
@@ -936,22 +950,15 @@ __device__ __forceinline__ void plan_body(
   static_assert(kPlanBins == kPlanThreads, "one bin per thread");
   static_assert(kPlanWaves <= kWave, "wave totals scanned by one wave");
 
-  // Inclusive scan of x over the block: within each wave by lane shuffles,
-  // then across the wave totals.  Returns this thread's inclusive prefix;
-  // *total receives the block total.
+  // Inclusive scan of x over the block: within each wave, then across the
+  // wave totals.  Returns this thread's inclusive prefix; *total receives the
+  // block total.
   auto block_scan = [&](int x, int* total) {
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int y = __shfl_up(x, d, kWave);
-      if (lane >= d) x += y;
-    }
+    x = wave_inclusive_sum(x);
     if (lane == kWave - 1) wave_sum[wave] = x;
     __syncthreads();
     if (wave == 0) {
-      int v = lane < kPlanWaves ? wave_sum[lane] : 0;
-      for (int d = 1; d < kPlanWaves; d <<= 1) {
-        const int y = __shfl_up(v, d, kWave);
-        if (lane >= d) v += y;
-      }
+      const int v = wave_inclusive_sum(lane < kPlanWaves ? wave_sum[lane] : 0);
       if (lane < kPlanWaves) wave_sum[lane] = v;
     }
     __syncthreads();
