@@ -218,3 +218,30 @@ def test_reduce_on_synthetic_partials(s_, lens):
                 ref = oracle.merge(m[b, h, :active].astype(np.float64) * math.log(2.0),
                                    l[b, h, :active], acc[b, h, :active]) if active else np.zeros(d)
                 assert_close(got[b, h], ref, dtype, f"reduce b={b} h={h}")
+
+
+def _random_decode_case(seed):
+    """A seeded random batch: group sizes 1 to 8, head_dim 64 or 128, bf16 or fp32, block
+    sizes 8 to 512, 1 to 12 sequences of 1 to 2500 positions, a split size that is a
+    random multiple of 64 up to 1024."""
+    rng = np.random.default_rng(9200 + seed)
+    hq, hkv = [(16, 8), (8, 8), (16, 4), (16, 2), (32, 4)][int(rng.integers(5))]
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    bs = int(rng.choice([8, 16, 32, 64, 128, 256, 512]))
+    nseq = int(rng.integers(1, 13))
+    lengths = rng.integers(1, 2501, size=nseq)
+    if nseq > 1:
+        lengths[int(rng.integers(nseq))] = 1
+    partition = 64 * int(rng.integers(1, 17))
+    case = W.decode_case(f"decode_rand_{seed}", 9200 + seed, lengths=lengths, hq=hq, hkv=hkv,
+                         d=d, dtype=dtype, bs=bs)
+    return case, partition
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_batches(seed):
+    """Seeded random batches (shapes, dtypes, block and split sizes, one-token contexts)
+    element by element against the oracle."""
+    case, partition = _random_decode_case(seed)
+    _decode_vs_oracle(case, partition)

@@ -267,3 +267,28 @@ def test_prefill_largest_supported_batch():
     seqs = sample_seqs(case, 32, seed=7)
     _, vals, out, _ = _prefill_vs_oracle(case, seqs=seqs)
     assert not torch.isnan(out.float()).any()
+
+
+def _random_prefill_case(seed):
+    """A seeded random batch: group sizes 1 to 8, head_dim 64 or 128, block sizes 16 to 256,
+    1 to 6 sequences of 1 to 700 positions, about 40% with an unaligned cached prefix and,
+    in half the batches, a decode row (one new position after its cached ones)."""
+    rng = np.random.default_rng(9100 + seed)
+    hq, hkv = [(16, 8), (8, 8), (16, 4), (16, 2), (32, 4)][int(rng.integers(5))]
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    nseq = int(rng.integers(1, 7))
+    lengths = rng.integers(1, 701, size=nseq)
+    cached = np.array([int(rng.integers(0, n)) if rng.random() < 0.4 else 0 for n in lengths])
+    if nseq > 1 and rng.random() < 0.5 and lengths[0] > 1:
+        cached[0] = lengths[0] - 1
+    return W.prefill_case(f"prefill_rand_{seed}", 9100 + seed, lengths=lengths, cached=cached,
+                          hq=hq, hkv=hkv, d=d, bs=bs)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_prefill_random_batches(seed):
+    """Seeded random batches (shapes, lengths, cached prefixes, decode rows) element by
+    element against the oracle; every key tile, the output staging of every wave count and
+    the work list's orders are exercised on shapes the fixed cases do not pick."""
+    _prefill_vs_oracle(_random_prefill_case(seed))

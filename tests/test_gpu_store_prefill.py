@@ -117,3 +117,14 @@ def test_store_prefill_strided_new_rows():
     assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), "strided fused != two-call"
     assert torch.equal(kc.view(torch.int16), kc_s.view(torch.int16)), "K pool"
     assert torch.equal(vc.view(torch.int16), vc_s.view(torch.int16)), "V pool"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_store_prefill_random_batches(seed):
+    """The seeded random batches of the prefill sweep (shapes, cached prefixes, decode rows),
+    in both pool layouts and, for every third seed, with 192-key ranges: fused equals
+    two-call bit for bit, the pools equal the oracle's store, the outputs the oracle's
+    attention."""
+    from test_gpu_prefill import _random_prefill_case
+    layout = "bhsd" if seed % 2 else "bshd"
+    check(_random_prefill_case(seed), layout, split_keys=192 if seed % 3 == 0 else 0)
