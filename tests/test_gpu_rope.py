@@ -165,3 +165,32 @@ def test_zero_tokens_is_a_no_op():
                              vals["v_cache"])
     torch.cuda.synchronize()
     assert np.array_equal(W.raw_numpy(vals["k_cache"], case.dtype), k_before)
+
+
+def _random_rope_case(seed):
+    """A seeded random step: head layouts (groups 1 to 7, fewer head slots than a pass up
+    to six passes), head_dim 64 or 128, bf16 or fp32, blocks 16 to 256, 1 to 5 sequences of
+    1 to 600 positions, half with a cached prefix; norm weights, padded rows and in-place Q
+    drawn too."""
+    rng = np.random.default_rng(9300 + seed)
+    hq, hkv = [(16, 8), (12, 2), (32, 8), (3, 1), (40, 8), (8, 8), (28, 4)][int(rng.integers(7))]
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    bs = int(rng.choice([16, 64, 256]))
+    nseq = int(rng.integers(1, 6))
+    lengths = rng.integers(1, 601, size=nseq)
+    cached = np.array([int(rng.integers(0, n)) if rng.random() < 0.5 else 0 for n in lengths])
+    case = W.prefill_case(f"rope_rand_{seed}", 9300 + seed, lengths=lengths, cached=cached,
+                          hq=hq, hkv=hkv, d=d, dtype=dtype, bs=bs)
+    # row pads keep the row stride a multiple of 16 bytes, as the entry point requires
+    opts = dict(use_norm=bool(rng.random() < 0.8), row_pad=int(rng.choice([0, 8, 64])),
+                in_place=bool(rng.random() < 0.3))
+    return case, opts
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_norm_rope_store_random(seed):
+    """Seeded random steps against the oracle: rotated Q and stored K within the bounds
+    above, V and every slot outside the step bit for bit."""
+    case, opts = _random_rope_case(seed)
+    run_case(case, **opts)

@@ -110,3 +110,23 @@ def test_store_full_size_changes_only_the_new_slots(name):
         changed = torch.nonzero((c != o).any(dim=1)).flatten()
         assert set(changed.tolist()) <= set(case.slot_mapping.tolist())
         assert torch.equal(c.index_select(0, slots), new.view(raw).reshape(len(slots), -1))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_store_random_batches(seed):
+    """Seeded random batches (kv heads 1 to 8, head_dim 64 or 128, bf16 or fp32, blocks 8 to
+    512, ragged lengths with cached prefixes): the pool equals the oracle's store bit for
+    bit, every slot outside the step untouched."""
+    rng = np.random.default_rng(9400 + seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    bs = int(rng.choice([8, 16, 32, 64, 128, 256, 512]))
+    nseq = int(rng.integers(1, 9))
+    lengths = rng.integers(1, 1201, size=nseq)
+    cached = np.array([int(rng.integers(0, n)) if rng.random() < 0.5 else 0 for n in lengths])
+    case = W.prefill_case(f"store_rand_{seed}", 9400 + seed, lengths=lengths, cached=cached,
+                          hq=2 * hkv, hkv=hkv, d=d, dtype=dtype, bs=bs)
+    print(f"store case={case.name} T={case.num_new_tokens} Hkv={hkv} d={d} {dtype} bs={bs}",
+          flush=True)
+    _store_and_compare(case, W.materialize(case, DEV))
